@@ -1,0 +1,96 @@
+"""Exact decoders of the storage formats the GPU path reads (oracle; test
+infrastructure only).
+
+bf16      : the upper 16 bits of an IEEE binary32.
+e4m3fn    : OCP 8-bit float, 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+            subnormals, no infinities, S.1111.111 is NaN, max 448.
+e2m1      : OCP 4-bit float, 1 sign, 2 exponent (bias 1), 1 mantissa bit;
+            magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+e8m0      : OCP MX shared scale, 2**(E-127); E = 255 is NaN.
+MXFP4     : e2m1 elements, two per byte (element 2i in the low nibble), one
+            e8m0 scale per 32 consecutive elements along the last dimension.
+
+Why these formats: [P1] section FP4 量化 says the indexer's QK path runs in FP4
+and that dequantising FP4 to FP8 loses nothing because fine-grained sub-block
+scales fit in FP8's range. A power-of-two (e8m0) scale makes that statement
+exactly true for e2m1 -> e4m3, which is why MXFP4 is the reading taken.
+"""
+import numpy as np
+
+
+def bf16_to_f64(bits):
+    """uint16 bf16 bit patterns -> float64 (exact)."""
+    u = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_to_f64(bits):
+    """uint8 OCP e4m3fn codes -> float64 (exact; NaN code -> nan)."""
+    b = np.asarray(bits).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    mant = (b & 0x7).astype(np.float64)
+    normal = (1.0 + mant / 8.0) * np.ldexp(1.0, (e - 7).astype(np.int64))
+    sub = (mant / 8.0) * 2.0 ** -6
+    v = np.where(e == 0, sub, normal)
+    v = np.where((e == 15) & ((b & 7) == 7), np.nan, v)
+    return sign * v
+
+
+def e2m1_to_f64(codes):
+    """4-bit e2m1 codes (0..15, one per array element) -> float64 (exact)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    mant = (c & 0x1).astype(np.float64)
+    normal = (1.0 + mant / 2.0) * np.ldexp(1.0, (e - 1).astype(np.int64))
+    sub = mant * 0.5
+    return sign * np.where(e == 0, sub, normal)
+
+
+def e8m0_to_f64(bits):
+    """uint8 e8m0 scale codes -> float64 powers of two (255 -> nan)."""
+    b = np.asarray(bits).astype(np.int64)
+    v = np.ldexp(1.0, b - 127)
+    return np.where(b == 255, np.nan, v)
+
+
+def unpack_fp4(packed):
+    """[..., n/2] uint8 -> [..., n] e2m1 codes; element 2i is the low nibble."""
+    p = np.asarray(packed).astype(np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mxfp4_to_f64(packed, scales):
+    """MXFP4 tensor -> float64.
+
+    packed: [..., n/2] uint8 (two e2m1 codes per byte); scales: [..., n/32]
+    uint8 e8m0. Element i of a row is e2m1(code_i) * 2**(scale[i // 32] - 127).
+    """
+    vals = e2m1_to_f64(unpack_fp4(packed))
+    s = e8m0_to_f64(scales)
+    n = vals.shape[-1]
+    assert s.shape[-1] * 32 == n, "one e8m0 scale per 32 elements"
+    return vals * np.repeat(s, 32, axis=-1)
+
+
+def f32_to_f64(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def decode(arr, fmt, scales=None):
+    """Decode a storage array by format name: 'f32', 'bf16', 'fp8', 'fp4'."""
+    if fmt == "f32":
+        return f32_to_f64(arr)
+    if fmt == "bf16":
+        return bf16_to_f64(np.asarray(arr).view(np.uint16))
+    if fmt == "fp8":
+        return e4m3fn_to_f64(np.asarray(arr).view(np.uint8))
+    if fmt == "fp4":
+        assert scales is not None
+        return mxfp4_to_f64(np.asarray(arr).view(np.uint8), np.asarray(scales).view(np.uint8))
+    raise ValueError(fmt)
