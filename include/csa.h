@@ -1,0 +1,200 @@
+/*
+ * csa.h — C ABI of the MI355X (gfx950) compressed-attention library.
+ *
+ * Hybrid compressed attention as described for DeepSeek-V4:
+ *   CSA: every m consecutive tokens' KV is folded into one compressed entry; a
+ *        light indexer scores the entries per query, a per-query top-k keeps k
+ *        of them, and attention runs over those plus a sliding window of raw
+ *        recent tokens, with partial RoPE and a per-head attention sink.
+ *   HCA: the same folding with m' = 128, attended densely (no top-k).
+ * Sources (page title, section):
+ *   [P1] "DeepSeek V4 重磅開源！首次打通華為Ascend，也沒丟掉英偉達，百萬上下文奪回國產模型話語權"
+ *        (InfoQ), section 拆解關鍵技術創新 -> 混合注意力機制 and FP4 量化.
+ *   [P3] 智猩猩 digest of "DeepSeek-V4: Towards Highly Efficient Million-Token
+ *        Context Intelligence" (aiorang.com), section 01 架构与基础设施优化.
+ * The pages do not define the compressor or the indexer; the forms computed
+ * here are stated at each entry point.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are caller-owned DEVICE memory, contiguous row-major
+ *    in the shapes given, 16-byte aligned. The library never allocates, frees,
+ *    synchronises or copies device-to-host; calls enqueue on `stream` (a
+ *    hipStream_t, NULL = the default stream) and return.
+ *  - Element formats (csa_dtype): CSA_F32 = float32; CSA_BF16 = bfloat16 bits
+ *    (uint16); CSA_FP8_E4M3 = OCP e4m3fn codes (uint8); CSA_FP4_E2M1 = MXFP4:
+ *    two e2m1 codes per byte (element 2i in the low nibble) plus one e8m0
+ *    scale byte (2^(E-127)) per 32 consecutive elements of the last dim.
+ *  - Positions: one shared KV head; the query row i of every sequence sits at
+ *    absolute position q_pos0 + i. Compressed entry j of a cache covers raw
+ *    positions j*m .. j*m+m-1 and is visible to a query at t iff j*m+m-1 <= t,
+ *    i.e. for j < n(t) = (t+1)/m.
+ *  - RoPE: on the last 64 dims of each head, interleaved pairs (2i, 2i+1),
+ *    frequency 10000^(-i/32), angle = position * frequency. Compressed keys are
+ *    stored rotated (at their block's last position); raw keys and queries are
+ *    stored unrotated and rotated inside the kernels.
+ *  - Errors: arguments are checked on the host before anything is enqueued; a
+ *    failed check returns a nonzero csa_status and launches nothing. A launch
+ *    failure returns CSA_ERR_LAUNCH. Faults inside a kernel surface at the
+ *    caller's next synchronisation.
+ *  - Workspaces: sized by the matching *_ws_bytes query. A workspace must be
+ *    zero-filled once when it is first allocated; every call leaves the parts
+ *    that must start at zero at zero again. Calls that share a workspace must
+ *    be ordered on one stream.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_F32 = 0,
+  CSA_BF16 = 1,
+  CSA_FP8_E4M3 = 2,
+  CSA_FP4_E2M1 = 3
+} csa_dtype;
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,       /* a required pointer is NULL */
+  CSA_ERR_SHAPE = 2,      /* a size or position is out of the supported range */
+  CSA_ERR_DTYPE = 3,      /* dtype not supported by this entry point */
+  CSA_ERR_ALIGN = 4,      /* a pointer is not 16-byte aligned */
+  CSA_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than the *_ws_bytes query */
+  CSA_ERR_LAUNCH = 6      /* the HIP runtime rejected a kernel launch */
+} csa_status;
+
+/* Version of this ABI (CSA_ABI_VERSION). */
+int csa_abi_version(void);
+
+/* Static, NUL-terminated description of a csa_status code. */
+const char* csa_strerror(int code);
+
+/*
+ * csa_compress — fold every m raw tokens' K and V into one compressed entry.
+ * [P1] 混合注意力機制: CSA compresses each m = 4 tokens' KV cache into one
+ * entry (sequence length 1/m); HCA uses m' = 128. Form taken (the pages give
+ * none): a softmax-gated weighted sum. For the block j of absolute positions
+ * s = j*m .. j*m+m-1:
+ *   g_s = <w_gate, K_raw[s]>,  alpha = softmax_s(g),
+ *   K_c[j] = RoPE(sum_s alpha_s K_raw[s], j*m+m-1),  V_c[j] = sum_s alpha_s V_raw[s].
+ *
+ *   B, T, D      sequences, raw tokens per sequence, head dim (128 or 512)
+ *   m            block size, 1..4096
+ *   pos0         absolute position of raw row 0; must be a multiple of m
+ *   kv_dtype     CSA_F32 or CSA_BF16 (raw and compressed rows alike)
+ *   k_raw, v_raw [B, T, D] unrotated keys, values
+ *   w_gate       [D] float32
+ *   k_c, v_c     [B, N_cap, D]; rows pos0/m .. pos0/m + T/m - 1 are written,
+ *                others untouched. A trailing partial block (T % m tokens)
+ *                produces nothing. Requires pos0/m + T/m <= N_cap.
+ */
+int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
+                 const void* k_raw, const void* v_raw, const float* w_gate,
+                 void* k_c, void* v_c, int64_t N_cap, void* stream);
+
+/*
+ * csa_index_topk — Lightning Indexer scores, then per-query top-k.
+ * [P1] 混合注意力機制: a light indexer picks the important compressed blocks
+ * and each query attends only k of them (k = 512..1024); [P1] FP4 量化: the
+ * indexer's QK path runs in FP4. Form taken (the pages give none):
+ *   I[t, j] = sum_h w_i[t, h] * max(0, <q_i[t, h, :], k_i[j, :]>),  j < n(t),
+ * accumulated in float32 (exact for small-integer inputs). Top-k: the key
+ * (-I, j) orders entries, so ties go to the lower j; -0 equals +0. The first
+ * min(k, n(t)) are written in ascending j, the remaining slots hold -1.
+ *
+ *   B, Lq, q_pos0  sequences, query rows per sequence, position of row 0
+ *   m              compression block of the cache being indexed (>= 1)
+ *   N_cap          rows of k_i per sequence; requires n(q_pos0+Lq-1) <= N_cap
+ *   H_i, d_i       indexer heads (4, 8, 16, 32, 64 or 128) and dim
+ *                  (32..256, a multiple of 32)
+ *   idx_dtype      CSA_F32, CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1
+ *   q_i            [B, Lq, H_i, d_i] (fp4: [B, Lq, H_i, d_i/2] bytes)
+ *   q_i_scale      fp4 only: [B, Lq, H_i, d_i/32] e8m0; otherwise NULL
+ *   w_i            [B, Lq, H_i] float32 head weights
+ *   k_i            [B, N_cap, d_i] (fp4: [B, N_cap, d_i/2] bytes)
+ *   k_i_scale      fp4 only: [B, N_cap, d_i/32] e8m0; otherwise NULL
+ *   topk           1..2048
+ *   idx_out        [B, Lq, topk] int32
+ *   ws, ws_bytes   workspace of csa_index_topk_ws_bytes(B, Lq, N_cap) bytes.
+ *                  After the call its first B*Lq*N_cap floats hold I[b, t, j]
+ *                  for the visible j (other entries unspecified).
+ */
+size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t N_cap);
+int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
+                   int H_i, int d_i, int idx_dtype,
+                   const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                   const void* k_i, const uint8_t* k_i_scale,
+                   int topk, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_topk — the top-k step of csa_index_topk alone, on caller scores.
+ * [P1] 混合注意力機制 (each query keeps k compressed entries). Same rule as
+ * csa_index_topk: key (-score, j), ascending-j output, -1 padding.
+ *
+ *   scores     [B, Lq, N_cap] float32; row (b, i) is read for j < n(q_pos0+i)
+ *              only, and those values must be finite.
+ *   idx_out    [B, Lq, topk] int32. No workspace.
+ */
+int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores,
+             int topk, int32_t* idx_out, void* stream);
+
+/*
+ * csa_sparse_attn — CSA attention over the selected compressed entries plus
+ * the sliding window, with attention sink.
+ * [P1] 混合注意力機制: each query attends its k selected entries; RoPE on the
+ * last 64 dims; a sliding-window branch over raw recent tokens; an attention
+ * sink lets the weights add up to less than one. Form taken: one softmax over
+ *   compressed rows {idx[t, :] >= 0} (keys stored rotated) and
+ *   window rows s = max(0, t-W+1) .. t (raw keys rotated at s),
+ *   logits <RoPE(q, t), key> / sqrt(D), sink z_h joining the denominator only:
+ *   out = sum_r e^(l_r - M) v_r / (e^(z_h - M) + sum_r e^(l_r - M)),
+ *   lse = M + ln(denominator). No source and no sink: out = 0, lse = -inf.
+ *
+ *   B, Lq, q_pos0  as above; H query heads (1..128), D head dim (128 or 512)
+ *   kv_dtype       CSA_F32 or CSA_BF16: q, k_c, v_c, k_raw, v_raw and out
+ *   q              [B, Lq, H, D] unrotated
+ *   N_cap, k_c, v_c  [B, N_cap, D] compressed cache (keys rotated)
+ *   topk, idx      [B, Lq, topk] int32; entries outside [0, N_cap) are ignored
+ *   T_raw, raw_pos0, k_raw, v_raw  [B, T_raw, D] raw rows at absolute
+ *                  positions raw_pos0 ..; must cover every window row:
+ *                  raw_pos0 <= max(0, q_pos0-W+1), q_pos0+Lq-1 < raw_pos0+T_raw
+ *   W              window, 0..1024
+ *   sink           [H] float32 or NULL (no sink)
+ *   out            [B, Lq, H, D] in kv_dtype;  lse [B, Lq, H] float32 or NULL
+ *   ws, ws_bytes   workspace of csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W)
+ */
+size_t csa_sparse_attn_ws_bytes(int B, int Lq, int H, int D, int topk, int W);
+int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype,
+                    const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                    int topk, const int32_t* idx,
+                    int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                    const float* sink, void* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_dense_attn — HCA attention: every visible compressed entry plus the
+ * sliding window, with attention sink.
+ * [P1] 混合注意力機制: HCA compresses 128 tokens into one entry and keeps
+ * dense attention. Same formula as csa_sparse_attn with the compressed rows
+ * j = 0 .. n(t)-1 of a cache built with block m. Requires n(q_pos0+Lq-1) <= N_cap.
+ * Arguments as in csa_sparse_attn; ws of hca_dense_attn_ws_bytes(B, Lq,
+ * q_pos0, m, H, D, W) bytes.
+ */
+size_t hca_dense_attn_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int W);
+int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype,
+                   const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                   int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                   const float* sink, void* out, float* lse,
+                   void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

@@ -1,0 +1,180 @@
+"""MI355X (gfx950) hybrid compressed attention: CSA and HCA.
+
+Thin Python binding of the C-ABI library libcsa.so (declared in include/csa.h).
+The functions here only marshal torch tensors (device pointers, sizes and the
+current HIP stream) into the C calls; every step of the computation runs in
+the library's HIP kernels. There is no fallback: if libcsa.so is missing or the
+tensors are not on a GPU, the calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa.so")
+
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
+IDX_FORMATS = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3, "fp4": CSA_FP4_E2M1}
+
+# (name, restype, argtypes) of every exported symbol
+_I, _L, _P, _Z = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+SIGNATURES = {
+    "csa_abi_version": (_I, []),
+    "csa_strerror": (ctypes.c_char_p, [_I]),
+    "csa_compress": (_I, [_I, _I, _I, _I, _L, _I, _P, _P, _P, _P, _P, _L, _P]),
+    "csa_index_topk_ws_bytes": (_Z, [_I, _I, _L]),
+    "csa_index_topk": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
+    "csa_topk": (_I, [_I, _I, _L, _I, _L, _P, _I, _P, _P]),
+    "csa_sparse_attn_ws_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "csa_sparse_attn": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
+                             _P, _P, _P, _P, _Z, _P]),
+    "hca_dense_attn_ws_bytes": (_Z, [_I, _I, _L, _I, _I, _I, _I]),
+    "hca_dense_attn": (_I, [_I, _I, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _L, _P, _P, _I,
+                            _P, _P, _P, _P, _Z, _P]),
+}
+
+_lib = None
+
+
+class CSAError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libcsa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CSAError("libcsa.so is not built (run __graft_entry__.build() or "
+                           "python -m long_context_attention_16_amd.build_lib)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise CSAError("csa call failed: %d (%s)" % (rc, lib().csa_strerror(rc).decode()))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CSAError("tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise CSAError("tensor is not contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _kv_dtype(t):
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise CSAError("KV tensors must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ws(nbytes, device):
+    return torch.zeros((max(16, int(nbytes)) + 15) // 16 * 4, dtype=torch.float32, device=device)
+
+
+# ------------------------------------------------------------------ compress
+def compress(k_raw, v_raw, w_gate, m, pos0, k_c, v_c):
+    """Fold [B, T, D] raw rows at absolute positions pos0.. into k_c, v_c
+    [B, N_cap, D] (rows pos0//m .. pos0//m + T//m - 1 are written)."""
+    B, T, D = k_raw.shape
+    _check(lib().csa_compress(B, T, D, m, pos0, _kv_dtype(k_raw), _ptr(k_raw), _ptr(v_raw),
+                              _ptr(w_gate), _ptr(k_c), _ptr(v_c), k_c.shape[1], _stream()))
+    return k_c, v_c
+
+
+# ---------------------------------------------------------- indexer + top-k
+def index_topk_ws_bytes(B, Lq, N_cap):
+    return lib().csa_index_topk_ws_bytes(B, Lq, N_cap)
+
+
+def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, ws=None, out=None):
+    """Indexer scores and per-query top-k.
+
+    q_i [B, Lq, H_i, d_i] (fp4: [..., d_i/2] bytes + q_scale [..., d_i/32]),
+    w_i [B, Lq, H_i] f32, k_i [B, N_cap, d_i] (fp4: bytes + k_scale).
+    fmt: 'f32' | 'bf16' | 'fp8' | 'fp4'. Returns idx [B, Lq, topk] int32; the
+    f32 scores are left in ws[: B*Lq*N_cap].
+    """
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if ws is None:
+        ws = _ws(index_topk_ws_bytes(B, Lq, N_cap), q_i.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk), dtype=torch.int32, device=q_i.device)
+    _check(lib().csa_index_topk(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
+                                _ptr(q_scale), _ptr(w_i), _ptr(k_i), _ptr(k_scale), topk, _ptr(out),
+                                _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def topk(scores, k, q_pos0, m, out=None):
+    """Top-k of caller scores [B, Lq, N_cap] f32 -> idx [B, Lq, k] int32."""
+    B, Lq, N_cap = scores.shape
+    if out is None:
+        out = torch.empty((B, Lq, k), dtype=torch.int32, device=scores.device)
+    _check(lib().csa_topk(B, Lq, q_pos0, m, N_cap, _ptr(scores), k, _ptr(out), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------- attention
+def sparse_attn_ws_bytes(B, Lq, H, D, topk, W):
+    return lib().csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W)
+
+
+def hca_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W):
+    return lib().hca_dense_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W)
+
+
+def _alloc_out(q, out, lse):
+    B, Lq, H, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Lq, H), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def sparse_attn(q, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink, q_pos0, ws=None, out=None, lse=None):
+    """CSA attention. q [B, Lq, H, D]; k_c, v_c [B, N_cap, D]; idx [B, Lq, k];
+    k_raw, v_raw [B, T_raw, D] at positions raw_pos0..; sink [H] f32 or None.
+    Returns (out [B, Lq, H, D], lse [B, Lq, H])."""
+    B, Lq, H, D = q.shape
+    topk_ = idx.shape[-1]
+    if ws is None:
+        ws = _ws(sparse_attn_ws_bytes(B, Lq, H, D, topk_, W), q.device)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().csa_sparse_attn(B, Lq, q_pos0, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c),
+                                 _ptr(v_c), topk_, _ptr(idx), k_raw.shape[1], raw_pos0, _ptr(k_raw),
+                                 _ptr(v_raw), W, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream()))
+    return out, lse
+
+
+def hca_attn(q, k_c, v_c, m, k_raw, v_raw, raw_pos0, W, sink, q_pos0, ws=None, out=None, lse=None):
+    """HCA attention over every visible entry (block m). Shapes as sparse_attn."""
+    B, Lq, H, D = q.shape
+    if ws is None:
+        ws = _ws(hca_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W), q.device)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().hca_dense_attn(B, Lq, q_pos0, m, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c),
+                                _ptr(v_c), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W,
+                                _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream()))
+    return out, lse

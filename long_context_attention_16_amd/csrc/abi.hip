@@ -1,0 +1,184 @@
+// C ABI of the library: argument checks on the host, then the launches.
+// Every check runs before anything is enqueued, allocates nothing and costs
+// well under a microsecond.
+#include "../../include/csa.h"
+#include "launch.hpp"
+
+using namespace csa;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool kv_ok(int dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+inline bool head_dim_ok(int D) { return D == 128 || D == 512; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Visible compressed entries of the last query row.
+inline int64_t n_last(int64_t q_pos0, int Lq, int m) { return (q_pos0 + Lq) / m; }
+
+int check_window(int Lq, int64_t q_pos0, int W, int T_raw, int64_t raw_pos0) {
+  if (W < 0 || W > 1024 || T_raw < 0) return CSA_ERR_SHAPE;
+  if (W == 0) return CSA_OK;
+  const int64_t lo = q_pos0 - W + 1 > 0 ? q_pos0 - W + 1 : 0;
+  if (raw_pos0 < 0 || raw_pos0 > lo) return CSA_ERR_SHAPE;
+  if (q_pos0 + Lq - 1 >= raw_pos0 + T_raw) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+int attn_nsplit_max_csa(int topk, int W) { return attn_nsplit(topk + W); }
+int attn_nsplit_max_hca(int64_t q_pos0, int Lq, int m, int W) {
+  return attn_nsplit((int)n_last(q_pos0, Lq, m) + W);
+}
+size_t attn_ws(int B, int Lq, int H, int D, int nsplit) {
+  if (nsplit <= 1) return 16;
+  const size_t slots = (size_t)B * Lq * nsplit * H;
+  return slots * D * 4 + slots * 2 * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_strerror(int code) {
+  switch (code) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL: return "a required pointer is NULL";
+    case CSA_ERR_SHAPE: return "a size or position is outside the supported range";
+    case CSA_ERR_DTYPE: return "dtype not supported by this entry point";
+    case CSA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
+                 const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
+                 void* stream) {
+  if (!k_raw || !v_raw || !w_gate || !k_c || !v_c) return CSA_ERR_NULL;
+  if (!kv_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (B < 0 || T < 0 || !head_dim_ok(D) || m < 1 || m > 4096 || pos0 < 0 || pos0 % m != 0 || N_cap < 0)
+    return CSA_ERR_SHAPE;
+  if (pos0 / m + T / m > N_cap) return CSA_ERR_SHAPE;
+  if (!aligned16(k_raw) || !aligned16(v_raw) || !aligned16(w_gate) || !aligned16(k_c) || !aligned16(v_c))
+    return CSA_ERR_ALIGN;
+  return launch_compress(B, T, D, m, pos0, kv_dtype, k_raw, v_raw, w_gate, k_c, v_c, N_cap,
+                         as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t N_cap) {
+  if (B <= 0 || Lq <= 0 || N_cap <= 0) return 16;
+  return (size_t)B * Lq * N_cap * sizeof(float);
+}
+
+static int check_topk_shape(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
+  if (B < 0 || Lq < 0 || q_pos0 < 0 || m < 1 || N_cap < 1 || topk < 1 || topk > 2048) return CSA_ERR_SHAPE;
+  if (n_last(q_pos0, Lq, m) > N_cap) return CSA_ERR_SHAPE;
+  if (N_cap > (int64_t)1 << 30) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                   int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                   const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!q_i || !w_i || !k_i || !idx_out) return CSA_ERR_NULL;
+  if (idx_dtype < CSA_F32 || idx_dtype > CSA_FP4_E2M1) return CSA_ERR_DTYPE;
+  if (idx_dtype == CSA_FP4_E2M1 && (!q_i_scale || !k_i_scale)) return CSA_ERR_NULL;
+  if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
+  if (!(H_i == 4 || H_i == 8 || H_i == 16 || H_i == 32 || H_i == 64 || H_i == 128)) return CSA_ERR_SHAPE;
+  if (!(d_i == 32 || d_i == 64 || d_i == 128)) return CSA_ERR_SHAPE;
+  if (!aligned16(q_i) || !aligned16(w_i) || !aligned16(k_i) || !aligned16(idx_out) || !aligned16(ws))
+    return CSA_ERR_ALIGN;
+  if (!ws || ws_bytes < csa_index_topk_ws_bytes(B, Lq, N_cap)) return CSA_ERR_WORKSPACE;
+  if ((int64_t)B * Lq == 0) return CSA_OK;
+  hipStream_t st = as_stream(stream);
+  float* scores = (float*)ws;
+  if (launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                      k_i_scale, scores, st))
+    return CSA_ERR_LAUNCH;
+  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, st) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
+             int32_t* idx_out, void* stream) {
+  if (!scores || !idx_out) return CSA_ERR_NULL;
+  if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
+  if (!aligned16(scores) || !aligned16(idx_out)) return CSA_ERR_ALIGN;
+  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, as_stream(stream)) ? CSA_ERR_LAUNCH
+                                                                                       : CSA_OK;
+}
+
+static int check_attn_common(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
+                             const void* k_c, const void* v_c, int T_raw, int64_t raw_pos0,
+                             const void* k_raw, const void* v_raw, int W, const float* sink,
+                             void* out, float* lse, void* ws, int64_t N_cap) {
+  if (!q || !k_c || !v_c || !out) return CSA_ERR_NULL;
+  if (W > 0 && (!k_raw || !v_raw)) return CSA_ERR_NULL;
+  if (!kv_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (B < 0 || Lq < 0 || q_pos0 < 0 || H < 1 || H > 128 || !head_dim_ok(D) || N_cap < 1) return CSA_ERR_SHAPE;
+  if (int rc = check_window(Lq, q_pos0, W, T_raw, raw_pos0)) return rc;
+  if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(out) || !aligned16(ws) ||
+      (W > 0 && (!aligned16(k_raw) || !aligned16(v_raw))))
+    return CSA_ERR_ALIGN;
+  (void)sink;
+  (void)lse;
+  return CSA_OK;
+}
+
+size_t csa_sparse_attn_ws_bytes(int B, int Lq, int H, int D, int topk, int W) {
+  if (B <= 0 || Lq <= 0 || topk < 0 || W < 0) return 16;
+  return attn_ws(B, Lq, H, D, attn_nsplit_max_csa(topk, W));
+}
+
+int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
+                    int64_t N_cap, const void* k_c, const void* v_c, int topk, const int32_t* idx,
+                    int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                    const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (topk > 0 && !idx) return CSA_ERR_NULL;
+  if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw,
+                                 v_raw, W, sink, out, lse, ws, N_cap))
+    return rc;
+  if (topk < 0 || topk > 2048) return CSA_ERR_SHAPE;
+  if (!ws || ws_bytes < csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W)) return CSA_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
+  a.k_c = k_c; a.v_c = v_c; a.topk = topk; a.idx = idx; a.T_raw = T_raw; a.raw_pos0 = raw_pos0;
+  a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
+  a.nsplit_max = attn_nsplit_max_csa(topk, W);
+  const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
+  a.ws_o = (float*)ws;
+  a.ws_ml = (float*)ws + slots * D;
+  return launch_attn(a, kv_dtype, false, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+size_t hca_dense_attn_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int W) {
+  if (B <= 0 || Lq <= 0 || m < 1 || W < 0 || q_pos0 < 0) return 16;
+  return attn_ws(B, Lq, H, D, attn_nsplit_max_hca(q_pos0, Lq, m, W));
+}
+
+int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype, const void* q,
+                   int64_t N_cap, const void* k_c, const void* v_c, int T_raw, int64_t raw_pos0,
+                   const void* k_raw, const void* v_raw, int W, const float* sink, void* out,
+                   float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw,
+                                 v_raw, W, sink, out, lse, ws, N_cap))
+    return rc;
+  if (m < 1 || m > 4096) return CSA_ERR_SHAPE;
+  if (n_last(q_pos0, Lq, m) > N_cap || n_last(q_pos0, Lq, m) + W > (int64_t)1 << 30) return CSA_ERR_SHAPE;
+  if (!ws || ws_bytes < hca_dense_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W)) return CSA_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = m; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
+  a.k_c = k_c; a.v_c = v_c; a.topk = 0; a.idx = nullptr; a.T_raw = T_raw; a.raw_pos0 = raw_pos0;
+  a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
+  a.nsplit_max = attn_nsplit_max_hca(q_pos0, Lq, m, W);
+  const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
+  a.ws_o = (float*)ws;
+  a.ws_ml = (float*)ws + slots * D;
+  return launch_attn(a, kv_dtype, true, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Host-side launchers of the kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace csa {
+
+// Arguments of the attention kernels (CSA gathered rows and HCA dense rows).
+struct AttnArgs {
+  int B, Lq;
+  int64_t q_pos0;
+  int m;             // HCA block (visible entries n(t) = (t+1)/m)
+  int H, D;
+  const void* q;
+  int64_t N_cap;
+  const void* k_c;
+  const void* v_c;
+  int topk;          // CSA only
+  const int32_t* idx;
+  int T_raw;
+  int64_t raw_pos0;
+  const void* k_raw;
+  const void* v_raw;
+  int W;
+  const float* sink;
+  void* out;
+  float* lse;
+  float* ws_o;       // split partials [B*Lq][nsplit_max][H][D]
+  float* ws_ml;      // split (max, sum) [B*Lq][nsplit_max][H][2]
+  int nsplit_max;
+};
+
+// Rows per split of a query with S sources: about S/32, a multiple of 32, at
+// least 64. A function of S alone, so the split structure never depends on the
+// batch.
+__host__ __device__ inline int attn_split_rows(int S) {
+  int ch = (S + 31) / 32;
+  ch = ((ch + 31) / 32) * 32;
+  return ch < 64 ? 64 : ch;
+}
+__host__ __device__ inline int attn_nsplit(int S) {
+  const int ch = attn_split_rows(S);
+  const int ns = (S + ch - 1) / ch;
+  return ns < 1 ? 1 : ns;
+}
+
+int launch_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
+                    const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
+                    hipStream_t stream);
+int launch_index_qk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
+                    const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
+                    const uint8_t* k_s, float* scores, hipStream_t stream);
+int launch_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
+                int32_t* idx_out, hipStream_t stream);
+int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t stream);
+
+}  // namespace csa
