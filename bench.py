@@ -1,0 +1,375 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-attention hot path on one MI355X.
+
+Default workload: one CSA decode step at 128K context, batch 32 — indexer
+scores (64 heads x 128 dims, bf16) over 32768 compressed entries per sequence,
+top-512 selection, then attention of 64 query heads (one KV head, head dim
+512) over the 512 selected entries plus a 128-token window with sinks.
+Throughput = query tokens per second of the whole step, inputs resident in
+HBM. Two independent input sets alternate between steps so the working set is
+larger than the 256 MB Infinity Cache.
+
+Other workloads (--workload): hca_decode (HCA at 1M context, batch 16),
+pair_1m (CSA with an MXFP4 indexer plus HCA at 1M context, batch 8) and
+indexer_fp8_prefill (the fp8 indexer of a 4096-token prefill chunk at 64K
+context with 64 heads x 128 dims).
+
+Prints one JSON line. The CPU baseline times the CPU oracle (test
+infrastructure) on a bounded sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="csa_decode",
+                    choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the CPU-oracle sample")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------
+class Timer:
+    """HIP events around each kernel call, on the stream the calls use."""
+
+    def __init__(self, torch, labels):
+        self.torch = torch
+        self.labels = labels
+        self.pairs = {l: [] for l in labels}
+
+    def wrap(self, label, fn, record):
+        if not record:
+            return fn()
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        r = fn()
+        e.record()
+        self.pairs[label].append((s, e))
+        return r
+
+    def mean_us(self, label):
+        p = self.pairs[label]
+        return 1000.0 * sum(s.elapsed_time(e) for s, e in p) / len(p) if p else None
+
+
+def csa_decode_setup(torch, csa, wl, shape, seeds, dev):
+    sets = []
+    for sd in seeds:
+        x = wl.make_inputs(shape, sd, device=dev)
+        B, Lq = shape.B, shape.Lq
+        x["scores"] = torch.empty((B, Lq, shape.N_cap), dtype=torch.float32, device=dev)
+        x["idx"] = torch.empty((B, Lq, shape.topk), dtype=torch.int32, device=dev)
+        nb = csa.sparse_attn_ws_bytes(B, Lq, shape.H, shape.D, shape.topk, shape.W)
+        x["ws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        x["out"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty((B, Lq, shape.H), dtype=torch.float32, device=dev)
+        sets.append(x)
+    return sets
+
+
+def csa_step(csa, shape, x, tm, record, prefix=""):
+    s = shape
+    tm.wrap(prefix + "index_qk", lambda: csa.index_scores(
+        x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
+        out=x["scores"]), record)
+    tm.wrap(prefix + "topk", lambda: csa.topk(x["scores"], s.topk, s.q_pos0, s.m, out=x["idx"]), record)
+    tm.wrap(prefix + "sparse_attn", lambda: csa.sparse_attn(
+        x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"],
+        s.q_pos0, ws=x["ws"], out=x["out"], lse=x["lse"]), record)
+
+
+def hca_setup(torch, csa, wl, shape, seeds, dev):
+    sets = []
+    for sd in seeds:
+        x = wl.make_inputs(shape, sd, device=dev)
+        nb = csa.hca_attn_ws_bytes(shape.B, shape.Lq, shape.q_pos0, shape.m, shape.H, shape.D, shape.W)
+        x["ws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        x["out"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty((shape.B, shape.Lq, shape.H), dtype=torch.float32, device=dev)
+        sets.append(x)
+    return sets
+
+
+def hca_step(csa, shape, x, tm, record, prefix=""):
+    s = shape
+    tm.wrap(prefix + "hca_attn", lambda: csa.hca_attn(
+        x["q"], x["k_c"], x["v_c"], s.m, x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"], s.q_pos0,
+        ws=x["ws"], out=x["out"], lse=x["lse"]), record)
+
+
+# ---------------------------------------------------------- algorithmic bytes
+def idx_row_bytes(s):
+    return {"bf16": 2, "fp8": 1, "f32": 4}.get(s.idx, 0) * s.d_I or (s.d_I // 2 + s.d_I // 32)
+
+
+def index_qk_bytes(s):
+    """k_I rows of visible entries + q_I + head weights + scores written once."""
+    vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
+    n_last = (s.q_pos0 + s.Lq) // s.m
+    kb = s.B * n_last * idx_row_bytes(s)
+    qb = s.B * s.Lq * s.H_I * idx_row_bytes(s)
+    return kb + qb + s.B * s.Lq * s.H_I * 4 + s.B * vis * 4
+
+
+def index_qk_flops(s):
+    vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
+    return 2.0 * s.H_I * s.d_I * s.B * vis
+
+
+def sparse_attn_bytes(s):
+    kvb = 2 if s.kv == "bf16" else 4
+    rows = s.topk + s.W
+    return s.B * s.Lq * (rows * 2 * s.D * kvb + 2 * s.H * s.D * kvb + s.H * 4 + s.topk * 4)
+
+
+def topk_bytes(s):
+    vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
+    return s.B * vis * 4 + s.B * s.Lq * s.topk * 4
+
+
+def hca_bytes(s):
+    kvb = 2 if s.kv == "bf16" else 4
+    n = (s.q_pos0 + 1) // s.m
+    return s.B * s.Lq * ((n + s.W) * 2 * s.D * kvb + 2 * s.H * s.D * kvb + s.H * 4)
+
+
+# ------------------------------------------------------------- CPU baseline
+def _oracle_query(s, x, b):
+    """Oracle seconds for query token b of workload s; copying the input rows it
+    reads from the GPU to the host is not timed."""
+    import numpy as np
+    import torch
+    from oracle import attention as oatt, formats, indexer as oidx, topk as otopk
+
+    def bf(t):
+        return formats.bf16_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+
+    t = s.q_pos0
+    n = (t + 1) // s.m
+    lo = max(0, t - s.W + 1)
+    pos = np.arange(lo, t + 1)
+    q = x["q"][b].cpu()
+    sink = x["sink"].cpu().numpy().astype(np.float64)
+    spent = 0.0
+    if s.H_I:
+        qi, wi = x["q_i"][b].cpu(), x["w_i"][b].cpu()
+        ki = x["k_i"][b][:n].cpu()
+        qs = x["q_i_scale"][b].cpu() if x["q_i_scale"] is not None else None
+        ks = x["k_i_scale"][b][:n].cpu() if x["k_i_scale"] is not None else None
+        t0 = time.perf_counter()
+        if s.idx == "fp4":
+            qd, kd = formats.mxfp4_to_f64(qi[0].numpy(), qs[0].numpy()), formats.mxfp4_to_f64(ki.numpy(), ks.numpy())
+        else:
+            qd, kd = bf(qi[0]), bf(ki)
+        sc = oidx.index_scores(qd, wi[0].numpy().astype(np.float64), kd)
+        sel = otopk.topk_select(sc, s.topk)
+        sel = sel[sel >= 0]
+        spent += time.perf_counter() - t0
+        rows = torch.from_numpy(sel).to(x["k_c"].device)
+        kc, vc = x["k_c"][b][rows].cpu(), x["v_c"][b][rows].cpu()
+    else:
+        kc, vc = x["k_c"][b][:n].cpu(), x["v_c"][b][:n].cpu()
+    kr = x["k_raw"][b][pos[0] - s.raw_pos0:pos[-1] + 1 - s.raw_pos0].cpu()
+    vr = x["v_raw"][b][pos[0] - s.raw_pos0:pos[-1] + 1 - s.raw_pos0].cpu()
+    t0 = time.perf_counter()
+    oatt.attend_one(bf(q[0]), t, bf(kc), bf(vc), bf(kr), pos, bf(vr), sink)
+    spent += time.perf_counter() - t0
+    return spent
+
+
+def cpu_baseline(wl_name, parts, seconds):
+    """Time the CPU oracle, as it stands, on whole query tokens of the same
+    workload (every layer of it) until `seconds` of oracle work have run."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:
+        cores = 1
+    B = parts[0][0].B
+    done, spent = 0, 0.0
+    while done < B and (done == 0 or spent < seconds):
+        for s, x in parts:
+            spent += _oracle_query(s, x, done)
+        done += 1
+    cpu = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(done / spent, 4), "unit": "query-tok/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d query tokens of %s, %.1f s of oracle work (numpy float64, BLAS threads %d; "
+                      "host has %d CPUs: %s)" % (done, B, wl_name, spent, cores, os.cpu_count(), cpu)}
+
+
+# -------------------------------------------------------------------- main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build measures one GPU's share of the work "
+              "(--gpus %d, WORLD_SIZE %d requested)." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_attention_16_amd as csa
+    from long_context_attention_16_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    csa.lib()
+
+    W = args.workload
+    if W == "csa_decode":
+        shapes = [("", wl.CFG2)]
+    elif W == "hca_decode":
+        shapes = [("", wl.CFG4)]
+    elif W == "pair_1m":
+        shapes = [("csa.", wl.CFG5_CSA), ("hca.", wl.CFG5_HCA)]
+    else:
+        shapes = [("", wl.CFG3M)]
+
+    sets = []
+    for prefix, s in shapes:
+        base = {"csa_decode": "2", "hca_decode": "4", "indexer_fp8_prefill": "3M"}.get(W)
+        base = base or ("5csa" if s.H_I else "5hca")
+        seeds = [wl.SEEDS[base], 1000 + wl.SEEDS[base]]
+        if s.H_I and W != "indexer_fp8_prefill":
+            sets.append(csa_decode_setup(torch, csa, wl, s, seeds, dev))
+        elif s.H_I:
+            xs = []
+            for sd in seeds:
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(sd)
+                x = wl.indexer_inputs(s, gen, dev)
+                x["scores"] = torch.empty((s.B, s.Lq, s.N_cap), dtype=torch.float32, device=dev)
+                xs.append(x)
+            sets.append(xs)
+        else:
+            sets.append(hca_setup(torch, csa, wl, s, seeds, dev))
+    torch.cuda.synchronize()
+
+    labels = []
+    for prefix, s in shapes:
+        if W == "indexer_fp8_prefill":
+            labels += [prefix + "index_qk"]
+        elif s.H_I:
+            labels += [prefix + "index_qk", prefix + "topk", prefix + "sparse_attn"]
+        else:
+            labels += [prefix + "hca_attn"]
+    tm = Timer(torch, labels)
+
+    def step(k, record):
+        for (prefix, s), xs in zip(shapes, sets):
+            x = xs[k % len(xs)]
+            if W == "indexer_fp8_prefill":
+                tm.wrap(prefix + "index_qk", lambda: csa.index_scores(
+                    x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
+                    out=x["scores"]), record)
+            elif s.H_I:
+                csa_step(csa, s, x, tm, record, prefix)
+            else:
+                hca_step(csa, s, x, tm, record, prefix)
+
+    for k in range(args.warmup):
+        step(k, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    breakdown = {l: round(tm.mean_us(l), 2) for l in labels}
+
+    main_shape = shapes[0][1]
+    queries = main_shape.B * main_shape.Lq
+    value = queries / (ms / 1000.0)
+    if W == "csa_decode":
+        metric, unit = "CSA decode query-tok/s @128K ctx", "query-tok/s"
+        dom = "index_qk"
+        dom_bytes = index_qk_bytes(main_shape)
+        roof = {"bound": "hbm", "achieved": dom_bytes / (breakdown[dom] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+        cfg = {"workload": main_shape.name, "batch": main_shape.B, "context": main_shape.q_pos0 + 1,
+               "compressed_entries": main_shape.N_cap, "heads": main_shape.H, "head_dim": main_shape.D,
+               "indexer": "%dx%d %s" % (main_shape.H_I, main_shape.d_I, main_shape.idx),
+               "topk": main_shape.topk, "window": main_shape.W}
+        step_bytes = index_qk_bytes(main_shape) + topk_bytes(main_shape) + sparse_attn_bytes(main_shape)
+    elif W == "hca_decode":
+        metric, unit = "HCA decode query-tok/s @1M ctx", "query-tok/s"
+        dom = "hca_attn"
+        dom_bytes = hca_bytes(main_shape)
+        roof = {"bound": "hbm", "achieved": dom_bytes / (breakdown[dom] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+        cfg = {"workload": main_shape.name, "batch": main_shape.B, "context": main_shape.q_pos0 + 1,
+               "compressed_entries": main_shape.N_cap, "m": main_shape.m, "heads": main_shape.H,
+               "head_dim": main_shape.D, "window": main_shape.W}
+        step_bytes = dom_bytes
+    elif W == "pair_1m":
+        metric, unit = "CSA+HCA layer-pair decode query-tok/s @1M ctx", "query-tok/s"
+        dom = "csa.index_qk"
+        dom_bytes = index_qk_bytes(main_shape)
+        roof = {"bound": "hbm", "achieved": dom_bytes / (breakdown[dom] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+        cfg = {"workload": "csa_hca_pair_1m_b8", "batch": main_shape.B, "context": main_shape.q_pos0 + 1,
+               "csa_entries": main_shape.N_cap, "hca_entries": wl.CFG5_HCA.N_cap,
+               "indexer": "%dx%d mxfp4" % (main_shape.H_I, main_shape.d_I), "topk": main_shape.topk,
+               "heads": main_shape.H, "head_dim": main_shape.D, "window": main_shape.W}
+        step_bytes = (index_qk_bytes(main_shape) + topk_bytes(main_shape) + sparse_attn_bytes(main_shape)
+                      + hca_bytes(wl.CFG5_HCA))
+    else:
+        metric, unit = "indexer fp8 prefill query-tok/s @64K ctx", "query-tok/s"
+        dom = "index_qk"
+        fl = index_qk_flops(main_shape)
+        roof = {"bound": "mfma", "achieved": fl / (breakdown[dom] * 1e-6) / 1e12,
+                "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s"}
+        cfg = {"workload": main_shape.name, "batch": main_shape.B, "query_chunk": main_shape.Lq,
+               "context": main_shape.q_pos0 + main_shape.Lq, "compressed_entries": main_shape.N_cap,
+               "indexer": "%dx%d fp8" % (main_shape.H_I, main_shape.d_I)}
+        step_bytes = index_qk_bytes(main_shape)
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
+
+    result = {
+        "metric": metric, "value": round(value, 1), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": main_shape.kv if W != "indexer_fp8_prefill" else "fp8",
+        "data": "synthetic (seeded N(0,1) caches and queries, random-init indexer; no weights or datasets)",
+        "config": cfg, "roofline": roof,
+        "breakdown_us": breakdown,
+        "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline and W != "indexer_fp8_prefill":
+        parts = [(s, xs[0]) for (prefix, s), xs in zip(shapes, sets)]
+        result["cpu_baseline"] = cpu_baseline(cfg["workload"], parts, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

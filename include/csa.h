@@ -36,10 +36,9 @@
  *    failed check returns a nonzero csa_status and launches nothing. A launch
  *    failure returns CSA_ERR_LAUNCH. Faults inside a kernel surface at the
  *    caller's next synchronisation.
- *  - Workspaces: sized by the matching *_ws_bytes query. A workspace must be
- *    zero-filled once when it is first allocated; every call leaves the parts
- *    that must start at zero at zero again. Calls that share a workspace must
- *    be ordered on one stream.
+ *  - Workspaces: device scratch sized by the matching *_ws_bytes query; no
+ *    initial contents are required. Calls that share a workspace must be
+ *    ordered on one stream.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -113,7 +112,7 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
  *   m              compression block of the cache being indexed (>= 1)
  *   N_cap          rows of k_i per sequence; requires n(q_pos0+Lq-1) <= N_cap
  *   H_i, d_i       indexer heads (4, 8, 16, 32, 64 or 128) and dim
- *                  (32..256, a multiple of 32)
+ *                  (32, 64 or 128)
  *   idx_dtype      CSA_F32, CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1
  *   q_i            [B, Lq, H_i, d_i] (fp4: [B, Lq, H_i, d_i/2] bytes)
  *   q_i_scale      fp4 only: [B, Lq, H_i, d_i/32] e8m0; otherwise NULL
@@ -132,6 +131,17 @@ int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
                    const void* q_i, const uint8_t* q_i_scale, const float* w_i,
                    const void* k_i, const uint8_t* k_i_scale,
                    int topk, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_index_scores — the indexer step of csa_index_topk alone.
+ * Same formula, arguments and limits as csa_index_topk, without the top-k:
+ * writes scores [B, Lq, N_cap] float32, I[b, t, j] for j < n(t); entries
+ * j >= n(t) are left untouched. No workspace.
+ */
+int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
+                     int H_i, int d_i, int idx_dtype,
+                     const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                     const void* k_i, const uint8_t* k_i_scale, float* scores, void* stream);
 
 /*
  * csa_topk — the top-k step of csa_index_topk alone, on caller scores.

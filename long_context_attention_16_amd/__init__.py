@@ -25,6 +25,7 @@ SIGNATURES = {
     "csa_compress": (_I, [_I, _I, _I, _I, _L, _I, _P, _P, _P, _P, _P, _L, _P]),
     "csa_index_topk_ws_bytes": (_Z, [_I, _I, _L]),
     "csa_index_topk": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
+    "csa_index_scores": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "csa_topk": (_I, [_I, _I, _L, _I, _L, _P, _I, _P, _P]),
     "csa_sparse_attn_ws_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
@@ -121,6 +122,19 @@ def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, 
     _check(lib().csa_index_topk(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
                                 _ptr(q_scale), _ptr(w_i), _ptr(k_i), _ptr(k_scale), topk, _ptr(out),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def index_scores(q_i, w_i, k_i, q_pos0, m, fmt, q_scale=None, k_scale=None, out=None):
+    """Indexer scores only: returns (or fills) scores [B, Lq, N_cap] float32;
+    entries not yet visible to a query are left untouched."""
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if out is None:
+        out = torch.full((B, Lq, N_cap), float("-inf"), dtype=torch.float32, device=q_i.device)
+    _check(lib().csa_index_scores(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
+                                  _ptr(q_scale), _ptr(w_i), _ptr(k_i), _ptr(k_scale), _ptr(out), _stream()))
     return out
 
 

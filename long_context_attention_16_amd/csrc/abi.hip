@@ -80,18 +80,40 @@ static int check_topk_shape(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
   return CSA_OK;
 }
 
-int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
-                   int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
-                   const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
-                   size_t ws_bytes, void* stream) {
-  if (!q_i || !w_i || !k_i || !idx_out) return CSA_ERR_NULL;
+static int check_indexer(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                         int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                         const void* k_i, const uint8_t* k_i_scale, int topk) {
+  if (!q_i || !w_i || !k_i) return CSA_ERR_NULL;
   if (idx_dtype < CSA_F32 || idx_dtype > CSA_FP4_E2M1) return CSA_ERR_DTYPE;
   if (idx_dtype == CSA_FP4_E2M1 && (!q_i_scale || !k_i_scale)) return CSA_ERR_NULL;
   if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
   if (!(H_i == 4 || H_i == 8 || H_i == 16 || H_i == 32 || H_i == 64 || H_i == 128)) return CSA_ERR_SHAPE;
   if (!(d_i == 32 || d_i == 64 || d_i == 128)) return CSA_ERR_SHAPE;
-  if (!aligned16(q_i) || !aligned16(w_i) || !aligned16(k_i) || !aligned16(idx_out) || !aligned16(ws))
-    return CSA_ERR_ALIGN;
+  if (!aligned16(q_i) || !aligned16(w_i) || !aligned16(k_i)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                     int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                     const void* k_i, const uint8_t* k_i_scale, float* scores, void* stream) {
+  if (!scores) return CSA_ERR_NULL;
+  if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                             k_i_scale, 1))
+    return rc;
+  if (!aligned16(scores)) return CSA_ERR_ALIGN;
+  return launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                         k_i_scale, scores, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                   int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                   const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!idx_out) return CSA_ERR_NULL;
+  if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                             k_i_scale, topk))
+    return rc;
+  if (!aligned16(idx_out) || !aligned16(ws)) return CSA_ERR_ALIGN;
   if (!ws || ws_bytes < csa_index_topk_ws_bytes(B, Lq, N_cap)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
   hipStream_t st = as_stream(stream);

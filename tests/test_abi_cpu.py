@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 11, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -88,6 +88,13 @@ def test_index_topk_rejects(lib):
     bad = list(base); bad[15] = None
     assert f(*bad) == WS
     assert lib.csa_topk(1, 4, 200, 4, 64, P, 3000, P, None) == SHAPE
+    g = lib.csa_index_scores
+    sb = [1, 4, 200, 4, 64, 4, 32, 1, P, None, P, P, None, P, None]
+    assert g(*sb[:13], None, None) == NULL
+    bad = list(sb); bad[13] = MIS
+    assert g(*bad) == ALIGN
+    bad = list(sb); bad[6] = 16
+    assert g(*bad) == SHAPE
 
 
 def test_attention_rejects(lib):
