@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="csa_decode",
                     choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run the 1 GiB copy (calibration run for HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target length of the CPU-oracle sample")
     return ap.parse_args()
@@ -76,6 +78,8 @@ def csa_decode_setup(torch, csa, wl, shape, seeds, dev):
         B, Lq = shape.B, shape.Lq
         x["scores"] = torch.empty((B, Lq, shape.N_cap), dtype=torch.float32, device=dev)
         x["idx"] = torch.empty((B, Lq, shape.topk), dtype=torch.int32, device=dev)
+        tb = csa.topk_ws_bytes(B, Lq, shape.q_pos0, shape.m, shape.topk)
+        x["topk_ws"] = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=dev)
         nb = csa.sparse_attn_ws_bytes(B, Lq, shape.H, shape.D, shape.topk, shape.W)
         x["ws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
         x["out"] = torch.empty_like(x["q"])
@@ -89,7 +93,8 @@ def csa_step(csa, shape, x, tm, record, prefix=""):
     tm.wrap(prefix + "index_qk", lambda: csa.index_scores(
         x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
         out=x["scores"]), record)
-    tm.wrap(prefix + "topk", lambda: csa.topk(x["scores"], s.topk, s.q_pos0, s.m, out=x["idx"]), record)
+    tm.wrap(prefix + "topk", lambda: csa.topk(x["scores"], s.topk, s.q_pos0, s.m, out=x["idx"],
+                                              ws=x["topk_ws"]), record)
     tm.wrap(prefix + "sparse_attn", lambda: csa.sparse_attn(
         x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"],
         s.q_pos0, ws=x["ws"], out=x["out"], lse=x["lse"]), record)
@@ -148,6 +153,24 @@ def hca_bytes(s):
     kvb = 2 if s.kv == "bf16" else 4
     n = (s.q_pos0 + 1) // s.m
     return s.B * s.Lq * ((n + s.W) * 2 * s.D * kvb + 2 * s.H * s.D * kvb + s.H * 4)
+
+
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+    """Read+write bandwidth of a plain device copy of nbytes (context for the
+    roofline, and the calibration kernel for HBM byte counters)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1000.0 / reps
+    del src, dst
+    return round(2 * nbytes / sec / 1e9, 1)
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -239,6 +262,10 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     csa.lib()
+
+    if args.copy_only:
+        print(json.dumps({"copy_gbs": copy_ceiling(torch, dev), "bytes_per_copy": 2 * (1 << 30)}), flush=True)
+        return
 
     W = args.workload
     if W == "csa_decode":
@@ -362,6 +389,7 @@ def main():
         "config": cfg, "roofline": roof,
         "breakdown_us": breakdown,
         "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
+        "copy_ceiling_gbs": copy_ceiling(torch, dev),
     }
     if not args.no_cpu_baseline and W != "indexer_fp8_prefill":
         parts = [(s, xs[0]) for (prefix, s), xs in zip(shapes, sets)]

@@ -121,11 +121,11 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
  *   k_i_scale      fp4 only: [B, N_cap, d_i/32] e8m0; otherwise NULL
  *   topk           1..2048
  *   idx_out        [B, Lq, topk] int32
- *   ws, ws_bytes   workspace of csa_index_topk_ws_bytes(B, Lq, N_cap) bytes.
- *                  After the call its first B*Lq*N_cap floats hold I[b, t, j]
- *                  for the visible j (other entries unspecified).
+ *   ws, ws_bytes   workspace of csa_index_topk_ws_bytes(B, Lq, q_pos0, m,
+ *                  N_cap, topk) bytes. After the call its first B*Lq*N_cap
+ *                  floats hold I[b, t, j] for the visible j (others unspecified).
  */
-size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t N_cap);
+size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk);
 int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
                    int H_i, int d_i, int idx_dtype,
                    const void* q_i, const uint8_t* q_i_scale, const float* w_i,
@@ -150,10 +150,13 @@ int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
  *
  *   scores     [B, Lq, N_cap] float32; row (b, i) is read for j < n(q_pos0+i)
  *              only, and those values must be finite.
- *   idx_out    [B, Lq, topk] int32. No workspace.
+ *   idx_out    [B, Lq, topk] int32
+ *   ws, ws_bytes  workspace of csa_topk_ws_bytes(B, Lq, q_pos0, m, topk) bytes
+ *              (candidate lists of rows longer than 8192 entries).
  */
+size_t csa_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int topk);
 int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores,
-             int topk, int32_t* idx_out, void* stream);
+             int topk, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa_sparse_attn — CSA attention over the selected compressed entries plus

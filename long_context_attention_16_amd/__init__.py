@@ -23,10 +23,11 @@ SIGNATURES = {
     "csa_abi_version": (_I, []),
     "csa_strerror": (ctypes.c_char_p, [_I]),
     "csa_compress": (_I, [_I, _I, _I, _I, _L, _I, _P, _P, _P, _P, _P, _L, _P]),
-    "csa_index_topk_ws_bytes": (_Z, [_I, _I, _L]),
+    "csa_index_topk_ws_bytes": (_Z, [_I, _I, _L, _I, _L, _I]),
+    "csa_topk_ws_bytes": (_Z, [_I, _I, _L, _I, _I]),
     "csa_index_topk": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "csa_index_scores": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
-    "csa_topk": (_I, [_I, _I, _L, _I, _L, _P, _I, _P, _P]),
+    "csa_topk": (_I, [_I, _I, _L, _I, _L, _P, _I, _P, _P, _Z, _P]),
     "csa_sparse_attn_ws_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
                              _P, _P, _P, _P, _Z, _P]),
@@ -100,8 +101,12 @@ def compress(k_raw, v_raw, w_gate, m, pos0, k_c, v_c):
 
 
 # ---------------------------------------------------------- indexer + top-k
-def index_topk_ws_bytes(B, Lq, N_cap):
-    return lib().csa_index_topk_ws_bytes(B, Lq, N_cap)
+def index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk):
+    return lib().csa_index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk)
+
+
+def topk_ws_bytes(B, Lq, q_pos0, m, topk):
+    return lib().csa_topk_ws_bytes(B, Lq, q_pos0, m, topk)
 
 
 def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, ws=None, out=None):
@@ -116,7 +121,7 @@ def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, 
     N_cap = k_i.shape[1]
     d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
     if ws is None:
-        ws = _ws(index_topk_ws_bytes(B, Lq, N_cap), q_i.device)
+        ws = _ws(index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk), q_i.device)
     if out is None:
         out = torch.empty((B, Lq, topk), dtype=torch.int32, device=q_i.device)
     _check(lib().csa_index_topk(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
@@ -138,12 +143,15 @@ def index_scores(q_i, w_i, k_i, q_pos0, m, fmt, q_scale=None, k_scale=None, out=
     return out
 
 
-def topk(scores, k, q_pos0, m, out=None):
+def topk(scores, k, q_pos0, m, out=None, ws=None):
     """Top-k of caller scores [B, Lq, N_cap] f32 -> idx [B, Lq, k] int32."""
     B, Lq, N_cap = scores.shape
     if out is None:
         out = torch.empty((B, Lq, k), dtype=torch.int32, device=scores.device)
-    _check(lib().csa_topk(B, Lq, q_pos0, m, N_cap, _ptr(scores), k, _ptr(out), _stream()))
+    if ws is None:
+        ws = _ws(topk_ws_bytes(B, Lq, q_pos0, m, k), scores.device)
+    _check(lib().csa_topk(B, Lq, q_pos0, m, N_cap, _ptr(scores), k, _ptr(out), _ptr(ws),
+                          ws.numel() * ws.element_size(), _stream()))
     return out
 
 

@@ -29,10 +29,11 @@ int attn_nsplit_max_csa(int topk, int W) { return attn_nsplit(topk + W); }
 int attn_nsplit_max_hca(int64_t q_pos0, int Lq, int m, int W) {
   return attn_nsplit((int)n_last(q_pos0, Lq, m) + W);
 }
-size_t attn_ws(int B, int Lq, int H, int D, int nsplit) {
+// Split partials: O in the KV dtype, then (max, sum) in f32.
+size_t attn_ws(int B, int Lq, int H, int D, int nsplit, int kv_bytes) {
   if (nsplit <= 1) return 16;
   const size_t slots = (size_t)B * Lq * nsplit * H;
-  return slots * D * 4 + slots * 2 * 4;
+  return (slots * D * kv_bytes + 15) / 16 * 16 + slots * 2 * 4;
 }
 
 }  // namespace
@@ -68,9 +69,19 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const v
                          as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
-size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t N_cap) {
+size_t csa_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
+  if (B <= 0 || Lq <= 0 || m < 1 || q_pos0 < 0 || topk < 1) return 16;
+  const size_t b = topk_ws_bytes(B, Lq, n_last(q_pos0, Lq, m), topk);
+  return b < 16 ? 16 : b;
+}
+
+static size_t scores_bytes(int B, int Lq, int64_t N_cap) {
+  return ((size_t)B * Lq * N_cap * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
   if (B <= 0 || Lq <= 0 || N_cap <= 0) return 16;
-  return (size_t)B * Lq * N_cap * sizeof(float);
+  return scores_bytes(B, Lq, N_cap) + csa_topk_ws_bytes(B, Lq, q_pos0, m, topk);
 }
 
 static int check_topk_shape(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
@@ -114,23 +125,25 @@ int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i,
                              k_i_scale, topk))
     return rc;
   if (!aligned16(idx_out) || !aligned16(ws)) return CSA_ERR_ALIGN;
-  if (!ws || ws_bytes < csa_index_topk_ws_bytes(B, Lq, N_cap)) return CSA_ERR_WORKSPACE;
+  if (!ws || ws_bytes < csa_index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
   hipStream_t st = as_stream(stream);
   float* scores = (float*)ws;
+  void* cand = (char*)ws + scores_bytes(B, Lq, N_cap);
   if (launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                       k_i_scale, scores, st))
     return CSA_ERR_LAUNCH;
-  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, st) ? CSA_ERR_LAUNCH : CSA_OK;
+  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, cand, st) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
-             int32_t* idx_out, void* stream) {
+             int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (!scores || !idx_out) return CSA_ERR_NULL;
   if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
-  if (!aligned16(scores) || !aligned16(idx_out)) return CSA_ERR_ALIGN;
-  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, as_stream(stream)) ? CSA_ERR_LAUNCH
-                                                                                       : CSA_OK;
+  if (!aligned16(scores) || !aligned16(idx_out) || !aligned16(ws)) return CSA_ERR_ALIGN;
+  if (!ws || ws_bytes < csa_topk_ws_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
+  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, ws, as_stream(stream))
+             ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 static int check_attn_common(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
@@ -152,7 +165,7 @@ static int check_attn_common(int B, int Lq, int64_t q_pos0, int H, int D, int kv
 
 size_t csa_sparse_attn_ws_bytes(int B, int Lq, int H, int D, int topk, int W) {
   if (B <= 0 || Lq <= 0 || topk < 0 || W < 0) return 16;
-  return attn_ws(B, Lq, H, D, attn_nsplit_max_csa(topk, W));
+  return attn_ws(B, Lq, H, D, attn_nsplit_max_csa(topk, W), 4);
 }
 
 int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
@@ -172,14 +185,14 @@ int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, c
   a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
   a.nsplit_max = attn_nsplit_max_csa(topk, W);
   const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
-  a.ws_o = (float*)ws;
-  a.ws_ml = (float*)ws + slots * D;
+  a.ws_o = ws;
+  a.ws_ml = (float*)((char*)ws + (slots * D * (kv_dtype == CSA_F32 ? 4 : 2) + 15) / 16 * 16);
   return launch_attn(a, kv_dtype, false, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 size_t hca_dense_attn_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int W) {
   if (B <= 0 || Lq <= 0 || m < 1 || W < 0 || q_pos0 < 0) return 16;
-  return attn_ws(B, Lq, H, D, attn_nsplit_max_hca(q_pos0, Lq, m, W));
+  return attn_ws(B, Lq, H, D, attn_nsplit_max_hca(q_pos0, Lq, m, W), 4);
 }
 
 int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype, const void* q,
@@ -198,8 +211,8 @@ int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dt
   a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
   a.nsplit_max = attn_nsplit_max_hca(q_pos0, Lq, m, W);
   const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
-  a.ws_o = (float*)ws;
-  a.ws_ml = (float*)ws + slots * D;
+  a.ws_o = ws;
+  a.ws_ml = (float*)((char*)ws + (slots * D * (kv_dtype == CSA_F32 ? 4 : 2) + 15) / 16 * 16);
   return launch_attn(a, kv_dtype, true, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 

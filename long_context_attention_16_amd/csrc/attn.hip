@@ -10,18 +10,21 @@
 // sink logit that joins only the denominator.
 //
 // Design (MQA: one KV head shared by H query heads):
-//  * one workgroup per (query, split of its source list); NW = ceil(H/16)
-//    waves, wave w owning heads 16w .. 16w+15;
-//  * 32 source rows per tile are gathered (CSA: rows named by idx; HCA:
-//    consecutive rows; window: raw rows, rotated while staged) into LDS. K is
-//    kept row-major; V is stored transposed with its rows permuted so that a
-//    lane's 8 PV k-values are one 16-byte LDS read;
+//  * one workgroup per (query, split of its source list), two waves per
+//    group of 16 heads: both compute the group's scores, each accumulates the
+//    output for one half of D (halving the accumulator registers so that two
+//    waves fit per SIMD);
+//  * 32 source rows per tile go straight from HBM into LDS (CSA: rows named
+//    by idx; HCA: consecutive rows; window: raw rows, then rotated in LDS),
+//    double-buffered so the next tile's loads fly while this one is used;
+//    V stays row-major and is read with the LDS transpose instruction;
 //  * S^T = K Q^T and O^T = V^T P^T on MFMA 16x16 (bf16: 16x16x32; f32:
 //    16x16x4), so a lane's accumulators all belong to one head and the online
 //    softmax rescale is one multiply per register;
 //  * the split count depends only on the query's own source count, never on
 //    the batch, so results are batch-invariant and deterministic; a separate
-//    combine kernel merges the splits in a fixed order.
+//    combine kernel merges the splits in a fixed order (bf16 inputs keep
+//    their split partials in bf16, halving that traffic).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -61,251 +64,404 @@ template <> struct Chunk<float> {
   }
 };
 
-// Rotate the pairs of a 16-byte chunk starting at dim d0 (RoPE at position pos).
-template <typename T, int D>
-__device__ __forceinline__ uint4 rope_chunk(uint4 raw, int d0, int64_t pos) {
-  if (d0 < D - kRopeDims) return raw;
-  float v[Chunk<T>::N];
-  Chunk<T>::unpack(raw, v);
-#pragma unroll
-  for (int e = 0; e < Chunk<T>::N; e += 2) {
-    const int pair = (d0 + e - (D - kRopeDims)) / 2;
-    float c, s;
-    rope_cos_sin(pos, rope_inv_freq(pair), &c, &s);
-    const float x0 = v[e], x1 = v[e + 1];
-    v[e] = x0 * c - x1 * s;
-    v[e + 1] = x0 * s + x1 * c;
+// LDS tile of 32 source rows: 1 KB lines (every wave load writes one line),
+// each followed by kPadB bytes so the K and V^T fragment reads spread over
+// the LDS banks.
+constexpr int kPadB = 32;
+constexpr int kLineB = 1024 + kPadB;
+constexpr int kMaxSplitRows = 128;  // CSA splits: at most 96 rows (k <= 2048, W <= 1024)
+
+// LDS offset of byte `byte` of tile row r (rows longer than a line continue
+// in the next line, after the pad).
+template <int ROWB>
+__device__ __forceinline__ int lds_pos(int r, int byte) {
+  const int b = r * ROWB + byte;
+  return (b >> 10) * kLineB + (b & 1023);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt not waited).
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
+}
+
+struct SplitInfo {
+  int64_t t, lo;
+  int b, n_c, n_w, s0, s1;
+};
+
+// Source of split row sp: kind 0 = masked, 1 = compressed entry, 2 = window
+// row at absolute position *pos; *src = element offset of the row.
+template <int D, bool HCA>
+__device__ __forceinline__ int row_source(const AttnArgs& p, const SplitInfo& si, const int* sidx, int sp,
+                                          int64_t* src, int64_t* pos) {
+  *src = 0;
+  *pos = 0;
+  if (sp >= si.s1) return 0;
+  if (sp < si.n_c) {
+    const int64_t j = HCA ? (int64_t)sp : (int64_t)sidx[sp - si.s0];
+    if (j < 0 || j >= p.N_cap) return 0;
+    *src = ((int64_t)si.b * p.N_cap + j) * D;
+    return 1;
   }
-  return Chunk<T>::pack(v);
+  const int w = sp - si.n_c;
+  if (w >= si.n_w) return 0;
+  *pos = si.lo + w;
+  *src = ((int64_t)si.b * p.T_raw + (*pos - p.raw_pos0)) * D;
+  return 2;
+}
+
+// Issue the direct-to-LDS loads of the tile starting at split row ts, and
+// record each row's kind and position. Every wave issues 2*NL/NW loads.
+template <typename T, int D, int NW, bool HCA>
+__device__ __forceinline__ void issue_tile(const AttnArgs& p, const SplitInfo& si, const int* sidx, int ts,
+                                           uint8_t* Ks, uint8_t* Vs, int* kind_out, int64_t* pos_out) {
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int NL = 32 * ROWB / 1024;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const uint8_t* kc = (const uint8_t*)p.k_c;
+  const uint8_t* vc = (const uint8_t*)p.v_c;
+  const uint8_t* kr = (const uint8_t*)p.k_raw;
+  const uint8_t* vr = (const uint8_t*)p.v_raw;
+#pragma unroll
+  for (int L = wave; L < NL; L += NW) {
+    const int byte = L * 1024 + lane * 16;
+    const int r = byte / ROWB;
+    const int in_row = byte % ROWB;
+    int64_t src, pos;
+    const int kind = row_source<D, HCA>(p, si, sidx, ts + r, &src, &pos);
+    if (in_row == 0) { kind_out[r] = kind; pos_out[r] = pos; }  // the lane holding the row start
+    const int64_t off = kind ? src * (int64_t)sizeof(T) + in_row : in_row;  // masked: row 0 (finite)
+    const uint8_t* ks = (kind == 2 ? kr : kc) + off;
+    const uint8_t* vs = (kind == 2 ? vr : vc) + off;
+    __builtin_amdgcn_global_load_lds((const void*)ks, (__attribute__((address_space(3))) void*)(Ks + L * kLineB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)vs, (__attribute__((address_space(3))) void*)(Vs + L * kLineB), 16, 0, 0);
+  }
+}
+
+// cos/sin of the tile's window rows (only rows of kind 2 are filled).
+__device__ __forceinline__ void rope_table(const int* kind, const int64_t* pos, float (*rc)[kRopePairs + 1],
+                                           float (*rs)[kRopePairs + 1], int nt_threads) {
+  for (int e = threadIdx.x; e < 32 * kRopePairs; e += nt_threads) {
+    const int r = e / kRopePairs, pr = e % kRopePairs;
+    if (kind[r] == 2) rope_cos_sin(pos[r], pr, &rc[r][pr], &rs[r][pr]);
+  }
+}
+
+// Rotate, in LDS, the last 64 dims of the tile's window rows.
+template <typename T, int D>
+__device__ __forceinline__ void rope_rows_lds(uint8_t* Ks, const int* kind, float (*rc)[kRopePairs + 1],
+                                              float (*rs)[kRopePairs + 1], int nt_threads) {
+  constexpr int ROWB = D * (int)sizeof(T);
+  for (int e = threadIdx.x; e < 32 * kRopePairs; e += nt_threads) {
+    const int r = e / kRopePairs, pr = e % kRopePairs;
+    if (kind[r] != 2) continue;
+    const int d = D - kRopeDims + 2 * pr;
+    const float c = rc[r][pr], sn = rs[r][pr];
+    if constexpr (sizeof(T) == 2) {
+      uint32_t* w = reinterpret_cast<uint32_t*>(Ks + lds_pos<ROWB>(r, d * 2));
+      const uint32_t v = *w;
+      const float x0 = bf16_bits_to_f32((uint16_t)(v & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(v >> 16));
+      *w = (uint32_t)f32_to_bf16_bits(x0 * c - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * c) << 16);
+    } else {
+      float2* w = reinterpret_cast<float2*>(Ks + lds_pos<ROWB>(r, d * 4));
+      const float2 v = *w;
+      *w = make_float2(v.x * c - v.y * sn, v.x * sn + v.y * c);
+    }
+  }
+}
+
+template <typename T, int D>
+struct AttnState {
+  static constexpr bool BF = sizeof(T) == 2;
+  typedef typename std::conditional<BF, bf16x8, float>::type QFrag;
+  static constexpr int QN = BF ? D / 32 : D / 4;
+  QFrag qf[QN];
+  f32x4 acc[D / 32];  // this wave's half of D
+  float m_run, l_run;
+};
+
+// S^T = K Q^T, online softmax, O^T += V^T P^T for one tile in LDS.
+template <typename T, int D>
+__device__ __forceinline__ void compute_tile(AttnState<T, D>& st, const uint8_t* Ks, const uint8_t* Vs,
+                                             const int* kind, float cscale, int dh) {
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int ROWB = D * (int)sizeof(T);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, l16 = lane % 16;
+  f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if constexpr (BF) {
+    constexpr int QN = D / 32;
+    constexpr int KB = QN < 8 ? QN : 8;  // k-steps per batch of fragment reads
+#pragma unroll
+    for (int s0 = 0; s0 < QN; s0 += KB) {
+      uint4 kf[2][KB];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int s = 0; s < KB; ++s)
+          kf[rt][s] = *reinterpret_cast<const uint4*>(Ks + lds_pos<ROWB>(16 * rt + l16, (32 * (s0 + s) + 8 * g) * 2));
+#pragma unroll
+      for (int s = 0; s < KB; ++s)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+          sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[rt][s]), st.qf[s0 + s],
+                                                              sacc[rt], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 8; ++u)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float2 kk = *reinterpret_cast<const float2*>(Ks + lds_pos<ROWB>(16 * rt + l16, (8 * u + 2 * g) * 4));
+        sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.x, st.qf[2 * u], sacc[rt], 0, 0, 0);
+        sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.y, st.qf[2 * u + 1], sacc[rt], 0, 0, 0);
+      }
+  }
+  float x[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = kind[16 * rt + 4 * g + r] != 0;
+      x[rt][r] = ok ? sacc[rt][r] * cscale : -INFINITY;
+      tmax = fmaxf(tmax, x[rt][r]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+  const float m_new = fmaxf(st.m_run, tmax);
+  const bool none = m_new == -INFINITY;
+  const float alpha = none ? 1.f : exp2f(st.m_run - m_new);
+  float psum = 0.f;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[rt][r] = none ? 0.f : exp2f(x[rt][r] - m_new);
+      psum += x[rt][r];
+    }
+  psum += __shfl_xor(psum, 16, kWave);
+  psum += __shfl_xor(psum, 32, kWave);
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= alpha;
+
+  const int dt0 = dh * (D / 32);  // first d-tile of this wave's half
+  if constexpr (BF) {
+    const float pv[8] = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, Chunk<uint16_t>::pack(pv));
+    // transposed LDS reads: lane (l16, g) gets column d of rows 4g..4g+3 and 16+4g..16+4g+3
+    const int j4 = l16 / 4, jm = l16 % 4;
+    const int off_a = lds_pos<ROWB>(4 * g + j4, jm * 8) + dt0 * 32;
+    const int off_b = lds_pos<ROWB>(16 + 4 * g + j4, jm * 8) + dt0 * 32;
+    constexpr int DB = D / 32 < 8 ? D / 32 : 8;  // d-tiles per batch of reads
+#pragma unroll
+    for (int d0 = 0; d0 < D / 32; d0 += DB) {
+      v4i16 lo4[DB], hi4[DB];
+#pragma unroll
+      for (int q = 0; q < DB; ++q) {
+        lo4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + off_a + (d0 + q) * 32));
+        hi4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + off_b + (d0 + q) * 32));
+      }
+#pragma unroll
+      for (int q = 0; q < DB; ++q) {
+        const short8_t vv = {lo4[q][0], lo4[q][1], lo4[q][2], lo4[q][3], hi4[q][0], hi4[q][1], hi4[q][2], hi4[q][3]};
+        st.acc[d0 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, st.acc[d0 + q], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vr_ = 16 * rt + 4 * g + r;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+          const float v = *reinterpret_cast<const float*>(Vs + lds_pos<ROWB>(vr_, 4 * (16 * (dt0 + dt) + l16)));
+          st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, x[rt][r], st.acc[dt], 0, 0, 0);
+        }
+      }
+  }
+}
+
+template <typename T, int D>
+constexpr bool attn_double_buffered(int nw) {
+  return 2 * (32 * D * (int)sizeof(T) / 1024) / nw <= 32 && 4 * (32 * D * (int)sizeof(T) / 1024) * kLineB <= 140 * 1024;
 }
 
 template <typename T, int D, int NW, bool HCA>
 __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   constexpr bool BF = sizeof(T) == 2;
   constexpr int NT = NW * kWave;
-  constexpr int KSTR = D + (BF ? 8 : 4);  // K row stride (elements)
-  constexpr int VTSTR = 36;               // bf16 V^T row stride: 32 rows + 4 pad
-  constexpr int VSTR = D + 4;             // f32 V row stride
-  constexpr int EPC = Chunk<T>::N;
-  constexpr int CPR = D / EPC;
-  __shared__ __attribute__((aligned(16))) T Ks[32 * KSTR];
-  __shared__ __attribute__((aligned(16))) T Vs[BF ? D * VTSTR : 32 * VSTR];
-  __shared__ int64_t row_off[32];
-  __shared__ int64_t row_pos[32];
-  __shared__ int row_kind[32];  // 0: no row (masked), 1: compressed entry, 2: raw window row
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int NL = 32 * ROWB / 1024;   // lines per tile
+  constexpr bool DBUF = attn_double_buffered<T, D>(NW);
+  constexpr int NBUF = DBUF ? 2 : 1;
+  constexpr int LOADS = 2 * NL / NW;     // vector-memory ops per wave per tile
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[NL * kLineB];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[DBUF ? NL * kLineB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs1[DBUF ? NL * kLineB : 16];
+  __shared__ float rc[NBUF][32][kRopePairs + 1], rs[NBUF][32][kRopePairs + 1];
+  __shared__ int kind[NBUF][32];
+  __shared__ int64_t rpos[NBUF][32];
+  __shared__ float qcos[kRopePairs], qsin[kRopePairs];
+  __shared__ int sidx[HCA ? 1 : kMaxSplitRows];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int g = lane / 16, l16 = lane % 16;
   const int qrow = blockIdx.x / p.nsplit_max;
   const int split = blockIdx.x % p.nsplit_max;
-  const int b = qrow / p.Lq, i = qrow % p.Lq;
-  const int64_t t = p.q_pos0 + i;
-  const int n_c = HCA ? (int)((t + 1) / p.m) : p.topk;
-  const int64_t lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;
-  const int n_w = p.W > 0 ? (int)(t - lo + 1) : 0;
-  const int S = n_c + p.W;
+  SplitInfo si;
+  si.b = qrow / p.Lq;
+  const int i = qrow % p.Lq;
+  si.t = p.q_pos0 + i;
+  si.n_c = HCA ? (int)((si.t + 1) / p.m) : p.topk;
+  si.lo = si.t - p.W + 1 > 0 ? si.t - p.W + 1 : 0;
+  si.n_w = p.W > 0 ? (int)(si.t - si.lo + 1) : 0;
+  const int S = si.n_c + p.W;
   const int CH = attn_split_rows(S);
   const int nsplit = attn_nsplit(S);
   if (split >= nsplit) return;
-  const int s0 = split * CH;
-  const int s1 = min(S, s0 + CH);
+  si.s0 = split * CH;
+  si.s1 = min(S, si.s0 + CH);
+  const int ntiles = (si.s1 - si.s0 + 31) / 32;
 
-  const int h = wave * 16 + l16;
+  // Prologue: the split's idx slots, the query's RoPE table; first tiles' loads.
+  if constexpr (!HCA) {
+    for (int r = tid; r < si.s1 - si.s0; r += NT) {
+      const int sp = si.s0 + r;
+      sidx[r] = sp < si.n_c ? p.idx[(int64_t)qrow * p.topk + sp] : -1;
+    }
+  }
+  if (tid < kRopePairs) rope_cos_sin(si.t, tid, &qcos[tid], &qsin[tid]);
+  __syncthreads();
+  // wave = (head group of 16, half of D): both halves compute the same S for
+  // their heads; each accumulates O for its own half of D
+  const int dh = wave & 1;
+  const int h = (wave >> 1) * 16 + l16;
   const bool hok = h < p.H;
   const T* qbase = (const T*)p.q + ((int64_t)qrow * p.H + (hok ? h : 0)) * D;
-
-  // Q fragments (B operand of S^T = K Q^T), rotated at t.
-  typedef typename std::conditional<BF, bf16x8, float>::type QFrag;
-  constexpr int QN = BF ? D / 32 : D / 4;
-  QFrag qf[QN];
+  AttnState<T, D> st;
+  // Q loads first: vmcnt completes in order, so waiting for them later does
+  // not wait for the tile loads issued after them.
+  constexpr int QL = BF ? D / 32 : D / 8;
+  typedef typename std::conditional<BF, uint4, float2>::type QRaw;
+  QRaw qraw[QL];
+#pragma unroll
+  for (int s = 0; s < QL; ++s)
+    qraw[s] = *reinterpret_cast<const QRaw*>(qbase + (BF ? 32 * s + 8 * g : 8 * s + 2 * g));
+  if (ntiles > 0) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0, Ks0, Vs0, kind[0], rpos[0]);
+  if (DBUF && ntiles > 1) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32, Ks1, Vs1, kind[NBUF - 1], rpos[NBUF - 1]);
   if constexpr (BF) {
 #pragma unroll
-    for (int s = 0; s < QN; ++s) {
+    for (int s = 0; s < QL; ++s) {
       const int d0 = 32 * s + 8 * g;
-      uint4 raw = hok ? *reinterpret_cast<const uint4*>(qbase + d0) : make_uint4(0, 0, 0, 0);
-      raw = rope_chunk<T, D>(raw, d0, t);
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
+      uint4 raw = hok ? qraw[s] : make_uint4(0, 0, 0, 0);
+      if (d0 >= D - kRopeDims) {
+        float v[8];
+        Chunk<uint16_t>::unpack(raw, v);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int pr = (d0 + e - (D - kRopeDims)) / 2;
+          const float c = qcos[pr], sn = qsin[pr], x0 = v[e], x1 = v[e + 1];
+          v[e] = x0 * c - x1 * sn;
+          v[e + 1] = x0 * sn + x1 * c;
+        }
+        raw = Chunk<uint16_t>::pack(v);
+      }
+      st.qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < D / 8; ++u) {
+    for (int u = 0; u < QL; ++u) {
       const int d0 = 8 * u + 2 * g;
-      float2 x = hok ? *reinterpret_cast<const float2*>(qbase + d0) : make_float2(0.f, 0.f);
+      float2 x = hok ? qraw[u] : make_float2(0.f, 0.f);
       if (d0 >= D - kRopeDims) {
-        float c, s;
-        rope_cos_sin(t, rope_inv_freq((d0 - (D - kRopeDims)) / 2), &c, &s);
-        const float x0 = x.x, x1 = x.y;
-        x.x = x0 * c - x1 * s;
-        x.y = x0 * s + x1 * c;
+        const int pr = (d0 - (D - kRopeDims)) / 2;
+        const float c = qcos[pr], sn = qsin[pr], x0 = x.x, x1 = x.y;
+        x.x = x0 * c - x1 * sn;
+        x.y = x0 * sn + x1 * c;
       }
-      qf[2 * u] = x.x;
-      qf[2 * u + 1] = x.y;
+      st.qf[2 * u] = x.x;
+      st.qf[2 * u + 1] = x.y;
     }
   }
-
+  __syncthreads();  // row kinds/positions of the first tiles are visible
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float cscale = kLog2e / sqrtf((float)D);
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const T* kc = (const T*)p.k_c;
-  const T* vc = (const T*)p.v_c;
-  const T* kr = (const T*)p.k_raw;
-  const T* vr = (const T*)p.v_raw;
-
-  for (int ts = s0; ts < s1; ts += 32) {
-    if (tid < 32) {
-      const int sp = ts + tid;
-      int kind = 0;
-      int64_t off = 0, pos = 0;
-      if (sp < s1) {
-        if (sp < n_c) {
-          const int64_t j = HCA ? (int64_t)sp : (int64_t)p.idx[(int64_t)qrow * p.topk + sp];
-          if (j >= 0 && j < p.N_cap) { kind = 1; off = ((int64_t)b * p.N_cap + j) * D; }
-        } else {
-          const int w = sp - n_c;
-          if (w < n_w) {
-            kind = 2;
-            pos = lo + w;
-            off = ((int64_t)b * p.T_raw + (pos - p.raw_pos0)) * D;
-          }
-        }
-      }
-      row_kind[tid] = kind;
-      row_off[tid] = off;
-      row_pos[tid] = pos;
-    }
+  // One tile: rope table while its loads fly, wait for them, rotate window
+  // rows in LDS, compute, then reuse the buffer for the tile two ahead.
+  auto step = [&](int tt, uint8_t* Kb, uint8_t* Vb, int bi) {
+    const int ts = si.s0 + 32 * tt;
+    const bool win = si.n_w > 0 && ts + 32 > si.n_c;
+    // kind/rpos of this buffer were written by issue_tile before a barrier
+    if (win) rope_table(kind[bi], rpos[bi], rc[bi], rs[bi], NT);
+    if (DBUF && tt + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-
-    for (int c = tid; c < 32 * CPR; c += NT) {
-      const int r = c / CPR;
-      const int d0 = (c % CPR) * EPC;
-      const int kind = row_kind[r];
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (kind) {
-        const int64_t off = row_off[r] + d0;
-        kv = *reinterpret_cast<const uint4*>((kind == 1 ? kc : kr) + off);
-        vv = *reinterpret_cast<const uint4*>((kind == 1 ? vc : vr) + off);
-        if (kind == 2) kv = rope_chunk<T, D>(kv, d0, row_pos[r]);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * KSTR + d0]) = kv;
-      if constexpr (BF) {
-        const int pr = 8 * ((r % 16) / 4) + 4 * (r / 16) + (r % 4);
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          Vs[(d0 + e) * VTSTR + pr] = (uint16_t)((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xFFFF));
-      } else {
-        *reinterpret_cast<uint4*>(&Vs[r * VSTR + d0]) = vv;
-      }
+    if (win) {
+      rope_rows_lds<T, D>(Kb, kind[bi], rc[bi], rs[bi], NT);
+      __syncthreads();
     }
+    compute_tile<T, D>(st, Kb, Vb, kind[bi], cscale, dh);
     __syncthreads();
-
-    // S^T tiles: rows 16*rt + (4g + r), column = head.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const T* krow = &Ks[(16 * rt + l16) * KSTR];
-      if constexpr (BF) {
-#pragma unroll
-        for (int s = 0; s < QN; ++s) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 32 * s + 8 * g);
-          sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc[rt], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < D / 8; ++u) {
-          const float2 kk = *reinterpret_cast<const float2*>(krow + 8 * u + 2 * g);
-          sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.x, qf[2 * u], sacc[rt], 0, 0, 0);
-          sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.y, qf[2 * u + 1], sacc[rt], 0, 0, 0);
-        }
-      }
-    }
-    float x[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = row_kind[16 * rt + 4 * g + r] != 0;
-        x[rt][r] = ok ? sacc[rt][r] * cscale : -INFINITY;
-        tmax = fmaxf(tmax, x[rt][r]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float m_new = fmaxf(m_run, tmax);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : exp2f(m_run - m_new);
-    float psum = 0.f;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[rt][r] = none ? 0.f : exp2f(x[rt][r] - m_new);
-        psum += x[rt][r];
-      }
-    psum += __shfl_xor(psum, 16, kWave);
-    psum += __shfl_xor(psum, 32, kWave);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
-
-    if constexpr (BF) {
-      const float pv[8] = {x[0][0], x[0][1], x[0][2], x[0][3], x[1][0], x[1][1], x[1][2], x[1][3]};
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, Chunk<uint16_t>::pack(pv));
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vs[(16 * dt + l16) * VTSTR + 8 * g]);
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[dt], 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float* vrow = reinterpret_cast<const float*>(&Vs[(16 * rt + 4 * g + r) * VSTR]);
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt)
-            acc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * dt + l16], x[rt][r], acc[dt], 0, 0, 0);
-        }
-    }
-    __syncthreads();
+    const int nxt = tt + NBUF;
+    if (nxt < ntiles) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32 * nxt, Kb, Vb, kind[bi], rpos[bi]);
+  };
+  for (int tt = 0; tt < ntiles; tt += NBUF) {
+    step(tt, Ks0, Vs0, 0);
+    if (DBUF && tt + 1 < ntiles) step(tt + 1, Ks1, Vs1, NBUF - 1);
   }
 
   if (!hok) return;
   if (nsplit == 1) {
     const float z2 = p.sink ? p.sink[h] * kLog2e : -INFINITY;
-    const float M = fmaxf(z2, m_run);
+    const float M = fmaxf(z2, st.m_run);
     float f = 0.f, lse2 = -INFINITY;
     if (M != -INFINITY) {
-      const float den = exp2f(z2 - M) + l_run * exp2f(m_run - M);
-      f = exp2f(m_run - M) / den;
+      const float den = exp2f(z2 - M) + st.l_run * exp2f(st.m_run - M);
+      f = exp2f(st.m_run - M) / den;
       lse2 = M + log2f(den);
     }
     T* orow = (T*)p.out + ((int64_t)qrow * p.H + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const int d = 16 * dt + 4 * g;
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int d = 16 * (dh * (D / 32) + dt) + 4 * g;
       if constexpr (BF) {
-        const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(acc[dt][0] * f) | ((uint32_t)f32_to_bf16_bits(acc[dt][1] * f) << 16);
-        const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(acc[dt][2] * f) | ((uint32_t)f32_to_bf16_bits(acc[dt][3] * f) << 16);
+        const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(st.acc[dt][0] * f) | ((uint32_t)f32_to_bf16_bits(st.acc[dt][1] * f) << 16);
+        const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(st.acc[dt][2] * f) | ((uint32_t)f32_to_bf16_bits(st.acc[dt][3] * f) << 16);
         *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo2, hi2);
       } else {
-        *reinterpret_cast<float4*>(orow + d) = make_float4(acc[dt][0] * f, acc[dt][1] * f, acc[dt][2] * f, acc[dt][3] * f);
+        *reinterpret_cast<float4*>(orow + d) = make_float4(st.acc[dt][0] * f, st.acc[dt][1] * f, st.acc[dt][2] * f, st.acc[dt][3] * f);
       }
     }
-    if (p.lse && g == 0) p.lse[(int64_t)qrow * p.H + h] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
+    if (p.lse && g == 0 && dh == 0) p.lse[(int64_t)qrow * p.H + h] = lse2 == -INFINITY ? -INFINITY : lse2 * kLn2;
   } else {
     const int64_t slot = ((int64_t)qrow * p.nsplit_max + split) * p.H + h;
-    float* po = p.ws_o + slot * D;
+    T* po = (T*)p.ws_o + slot * D + dh * (D / 2);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (g == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(m_run, l_run);
+    for (int dt = 0; dt < D / 32; ++dt) {
+      if constexpr (BF) {
+        const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(st.acc[dt][0]) | ((uint32_t)f32_to_bf16_bits(st.acc[dt][1]) << 16);
+        const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(st.acc[dt][2]) | ((uint32_t)f32_to_bf16_bits(st.acc[dt][3]) << 16);
+        *reinterpret_cast<uint2*>(po + 16 * dt + 4 * g) = make_uint2(lo2, hi2);
+      } else {
+        *reinterpret_cast<float4*>(po + 16 * dt + 4 * g) = make_float4(st.acc[dt][0], st.acc[dt][1], st.acc[dt][2], st.acc[dt][3]);
+      }
+    }
+    if (g == 0 && dh == 0) *reinterpret_cast<float2*>(p.ws_ml + slot * 2) = make_float2(st.m_run, st.l_run);
   }
 }
 
@@ -340,7 +496,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs p) {
         const int64_t slot = slot0 + (int64_t)s * p.H;
         const float ms = p.ws_ml[slot * 2];
         const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M) * inv;
-        const float4 v = *reinterpret_cast<const float4*>(p.ws_o + slot * D + d);
+        float4 v;
+        if constexpr (sizeof(T) == 2) {
+          const uint2 r = *reinterpret_cast<const uint2*>((const T*)p.ws_o + slot * D + d);
+          v = make_float4(bf16_bits_to_f32((uint16_t)(r.x & 0xFFFF)), bf16_bits_to_f32((uint16_t)(r.x >> 16)),
+                          bf16_bits_to_f32((uint16_t)(r.y & 0xFFFF)), bf16_bits_to_f32((uint16_t)(r.y >> 16)));
+        } else {
+          v = *reinterpret_cast<const float4*>((const float*)p.ws_o + slot * D + d);
+        }
         o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
         o[2] = fmaf(wgt, v.z, o[2]); o[3] = fmaf(wgt, v.w, o[3]);
       }
@@ -359,13 +522,13 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs p) {
 
 template <typename T, int D, bool HCA>
 static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  const int nw = (a.H + 15) / 16;
+  const int hg = (a.H + 15) / 16;  // head groups; two waves (halves of D) per group
   const dim3 grid((unsigned)((int64_t)a.B * a.Lq * a.nsplit_max));
 #define CSA_ATTN_NW(N) hipLaunchKernelGGL((attn_kernel<T, D, N, HCA>), grid, dim3(N * kWave), 0, st, a)
-  if (nw == 1) CSA_ATTN_NW(1);
-  else if (nw == 2) CSA_ATTN_NW(2);
-  else if (nw <= 4) CSA_ATTN_NW(4);
-  else CSA_ATTN_NW(8);
+  if (hg == 1) CSA_ATTN_NW(2);
+  else if (hg == 2) CSA_ATTN_NW(4);
+  else if (hg <= 4) CSA_ATTN_NW(8);
+  else CSA_ATTN_NW(16);
 #undef CSA_ATTN_NW
   if (a.nsplit_max > 1)
     hipLaunchKernelGGL((attn_combine_kernel<T, D, HCA>), dim3((unsigned)((int64_t)a.B * a.Lq * a.H)),

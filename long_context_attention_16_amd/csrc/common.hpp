@@ -52,23 +52,37 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------- RoPE
-// Frequency of rotated pair i (0..31): 10000^(-i/32), in double.
-__device__ __forceinline__ double rope_inv_freq(int i) {
-  // log2(10000) = 13.287712379549449
-  return exp2(-(double)i * (13.287712379549449 / 32.0));
+// RoPE frequency of rotated pair i in revolutions per position:
+// 10000^(-i/32) / (2*pi), evaluated in double at compile time.
+constexpr double cexp_small(double x) {  // e^x for |x| <= 0.2 (Taylor, 24 terms)
+  double term = 1.0, sum = 1.0;
+  for (int k = 1; k < 24; ++k) { term *= x / k; sum += term; }
+  return sum;
 }
-// cos/sin of p * theta with the product and the reduction mod 2*pi in double,
-// so positions up to 2^20 keep full float accuracy.
-__device__ __forceinline__ void rope_cos_sin(int64_t p, double theta, float* c, float* s) {
-  const double two_pi = 6.283185307179586476925;
-  double a = (double)p * theta;
-  double k = rint(a * (1.0 / two_pi));
-  double r = fma(-k, two_pi, a);
-  // second term of 2*pi (Cody-Waite) keeps the reduced angle exact to ~1e-16
-  r = fma(-k, 2.4492935982947064e-16, r);
-  float rf = (float)r;
-  *s = sinf(rf);
-  *c = cosf(rf);
+constexpr double cexp(double x) {  // e^x for -16 <= x <= 0: e^(x/128)^128
+  double y = cexp_small(x / 128.0);
+  for (int k = 0; k < 7; ++k) y *= y;
+  return y;
+}
+constexpr double kLn10000 = 9.210340371976184;
+constexpr double kTwoPi = 6.283185307179586476925;
+constexpr double rope_rev(int i) { return cexp(-(double)i / 32.0 * kLn10000) / kTwoPi; }
+__constant__ const double kRopeRev[32] = {
+    rope_rev(0),  rope_rev(1),  rope_rev(2),  rope_rev(3),  rope_rev(4),  rope_rev(5),  rope_rev(6),
+    rope_rev(7),  rope_rev(8),  rope_rev(9),  rope_rev(10), rope_rev(11), rope_rev(12), rope_rev(13),
+    rope_rev(14), rope_rev(15), rope_rev(16), rope_rev(17), rope_rev(18), rope_rev(19), rope_rev(20),
+    rope_rev(21), rope_rev(22), rope_rev(23), rope_rev(24), rope_rev(25), rope_rev(26), rope_rev(27),
+    rope_rev(28), rope_rev(29), rope_rev(30), rope_rev(31)};
+
+// cos/sin of position p times the frequency of pair i. The angle is reduced
+// to a fraction of a revolution in double (exact to ~1e-11 rad for positions
+// up to 2^20), then evaluated in float on [-pi, pi].
+__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* s) {
+  const double a = (double)p * kRopeRev[i];
+  const float r = (float)(a - rint(a));
+  const float x = r * 6.2831853071795865f;
+  *s = sinf(x);
+  *c = cosf(x);
 }
 
 // ---------------------------------------------------------------- top-k keys

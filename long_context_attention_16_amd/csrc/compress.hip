@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_kernel(
     for (int e = 0; e < VEC; e += 2) {
       const int pair = (c0 + e - (D - kRopeDims)) / 2;
       float cs, sn;
-      rope_cos_sin(p, rope_inv_freq(pair), &cs, &sn);
+      rope_cos_sin(p, pair, &cs, &sn);
       const float x0 = ak[e], x1 = ak[e + 1];
       ak[e] = x0 * cs - x1 * sn;
       ak[e + 1] = x0 * sn + x1 * cs;

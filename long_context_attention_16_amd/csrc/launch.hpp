@@ -26,18 +26,19 @@ struct AttnArgs {
   const float* sink;
   void* out;
   float* lse;
-  float* ws_o;       // split partials [B*Lq][nsplit_max][H][D]
+  void* ws_o;        // split partials [B*Lq][nsplit_max][H][D], KV dtype (bf16 or f32)
   float* ws_ml;      // split (max, sum) [B*Lq][nsplit_max][H][2]
   int nsplit_max;
 };
 
-// Rows per split of a query with S sources: about S/32, a multiple of 32, at
-// least 64. A function of S alone, so the split structure never depends on the
-// batch.
+// Rows per split of a query with S sources: S/16 rounded up to a multiple of
+// 32, at least 96 (three 32-row tiles, so each workgroup pipelines loads with
+// compute). A function of S alone, so the split structure never depends on
+// the batch.
 __host__ __device__ inline int attn_split_rows(int S) {
-  int ch = (S + 31) / 32;
+  int ch = (S + 15) / 16;
   ch = ((ch + 31) / 32) * 32;
-  return ch < 64 ? 64 : ch;
+  return ch < 96 ? 96 : ch;
 }
 __host__ __device__ inline int attn_nsplit(int S) {
   const int ch = attn_split_rows(S);
@@ -51,8 +52,9 @@ int launch_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, cons
 int launch_index_qk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
                     const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
                     const uint8_t* k_s, float* scores, hipStream_t stream);
+size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk);
 int launch_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
-                int32_t* idx_out, hipStream_t stream);
+                int32_t* idx_out, void* ws, hipStream_t stream);
 int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t stream);
 
 }  // namespace csa

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 11, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -43,9 +43,15 @@ def test_version_and_strerror(lib):
 
 
 def test_ws_queries(lib):
-    assert lib.csa_index_topk_ws_bytes(32, 1, 32768) == 32 * 32768 * 4
-    # 640 sources -> 10 splits of 64 rows; partial O + (max, sum) per split and head
-    assert lib.csa_sparse_attn_ws_bytes(32, 1, 64, 512, 512, 128) == 32 * 10 * 64 * (512 + 2) * 4
+    # rows of at most 32768 entries: scores only (+16 for the empty candidate area)
+    assert lib.csa_index_topk_ws_bytes(32, 1, 131071, 4, 32768, 512) == 32 * 32768 * 4 + 16
+    # 262144 entries: 8 chunk lists of 1024 (key, index), then one merged list
+    assert lib.csa_topk_ws_bytes(8, 1, 1048575, 4, 1024) == 8 * 8 * 1024 * 8 + 8 * 1 * 1024 * 8
+    # rows of at most one chunk need no candidate lists
+    assert lib.csa_topk_ws_bytes(1, 4, 200, 4, 16) == 16
+    assert lib.csa_index_topk_ws_bytes(1, 4, 200, 4, 64, 16) == 1024 + 16
+    # 640 sources -> 7 splits of 96 rows; partial O + (max, sum) per split and head
+    assert lib.csa_sparse_attn_ws_bytes(32, 1, 64, 512, 512, 128) == 32 * 7 * 64 * (512 + 2) * 4
     # one split needs no partials
     assert lib.csa_sparse_attn_ws_bytes(1, 1, 4, 128, 16, 16) == 16
     assert lib.hca_dense_attn_ws_bytes(16, 1, 1048575, 128, 64, 512, 128) > 0
@@ -69,7 +75,7 @@ def test_compress_rejects(lib):
 
 def test_index_topk_rejects(lib):
     f = lib.csa_index_topk
-    n = lib.csa_index_topk_ws_bytes(1, 4, 64)
+    n = lib.csa_index_topk_ws_bytes(1, 4, 200, 4, 64, 8)
     base = [1, 4, 200, 4, 64, 4, 32, 1, P, None, P, P, None, 8, P, P, n, None]
     bad = list(base); bad[5] = 12
     assert f(*bad) == SHAPE                       # H_i not supported
@@ -87,7 +93,8 @@ def test_index_topk_rejects(lib):
     assert f(*bad) == WS
     bad = list(base); bad[15] = None
     assert f(*bad) == WS
-    assert lib.csa_topk(1, 4, 200, 4, 64, P, 3000, P, None) == SHAPE
+    assert lib.csa_topk(1, 4, 200, 4, 64, P, 3000, P, P, 16, None) == SHAPE
+    assert lib.csa_topk(1, 4, 200, 4, 64, P, 16, P, None, 16, None) == WS
     g = lib.csa_index_scores
     sb = [1, 4, 200, 4, 64, 4, 32, 1, P, None, P, P, None, P, None]
     assert g(*sb[:13], None, None) == NULL

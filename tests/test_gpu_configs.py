@@ -50,7 +50,7 @@ def _oracle_scores_row(s, x, b, i):
 
 
 def _run_csa(s, x):
-    ws = torch.empty(csa.index_topk_ws_bytes(s.B, s.Lq, s.N_cap) // 4 + 4, device=DEV)
+    ws = torch.empty(csa.index_topk_ws_bytes(s.B, s.Lq, s.q_pos0, s.m, s.N_cap, s.topk) // 4 + 4, device=DEV)
     idx = csa.index_topk(x["q_i"], x["w_i"], x["k_i"], s.topk, s.q_pos0, s.m, s.idx,
                          x["q_i_scale"], x["k_i_scale"], ws=ws)
     out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], idx, x["k_raw"], x["v_raw"], s.raw_pos0, s.W,

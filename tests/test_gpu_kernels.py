@@ -71,7 +71,7 @@ def test_index_scores_and_topk_exact(fmt, H_i, d_i):
     B, Lq, m, q_pos0, topk = 2, 21, 4, 4000, 100
     N_cap = (q_pos0 + Lq) // m + 3           # 1009: ragged against 32-entry tiles
     x = _exact_indexer(B, Lq, H_i, d_i, N_cap, fmt, seed=H_i * 7 + d_i)
-    ws = torch.zeros(csa.index_topk_ws_bytes(B, Lq, N_cap) // 4 + 4, device=DEV)
+    ws = torch.zeros(csa.index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk) // 4 + 4, device=DEV)
     idx = csa.index_topk(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, fmt,
                          x["q_i_scale"], x["k_i_scale"], ws=ws)
     torch.cuda.synchronize()
@@ -99,8 +99,10 @@ def _topk_case(scores, k, q_pos0, m):
     (40, 7, (-1.0, -0.0, 0.0, 1.0)),          # heavy ties and signed zeros
     (3000, 64, (-2.0, -1.0, 0.0, 1.0, 2.0)),
     (32768, 512, None),                        # decode shape, keys in LDS
-    (33000, 1024, (0.0, 1.0)),                 # beyond LDS: keys from global, 2 rounds
+    (33000, 1024, (0.0, 1.0)),                 # 5 chunks, ties across chunks
     (70000, 1024, None),
+    (327680, 1024, None),                      # 40960 candidates: merge reads global keys
+    (300000, 2048, (0.0, 1.0)),                # 75776 candidates, 3 compaction rounds, ties
 ])
 def test_topk(N, k, vals):
     rng = np.random.default_rng(N + k)
@@ -111,6 +113,20 @@ def test_topk(N, k, vals):
     else:
         s = rng.choice(np.array(vals, dtype=np.float32), size=(B, Lq, N))
     _topk_case(s, k, q_pos0, m)
+
+
+def test_topk_multichunk_ragged_rows():
+    """One launch whose first rows see fewer than k entries and whose last
+    rows span two chunks (rows checked by sampling)."""
+    rng = np.random.default_rng(8)
+    Lq, k, q_pos0 = 6300, 2048, 1999               # n = 2000 .. 8299
+    s = rng.integers(-3, 4, size=(1, Lq, 8300)).astype(np.float32)
+    t = torch.from_numpy(s).to(DEV)
+    idx = csa.topk(t, k, q_pos0, 1).cpu().numpy()
+    for i in (0, 1, 47, 2000, 6191, 6192, 6250, 6299):
+        n = q_pos0 + i + 1
+        want = otopk.topk_select(s[0, i, :n].astype(np.float64), k)
+        assert np.array_equal(idx[0, i], want), i
 
 
 def test_topk_small_n_and_padding():
