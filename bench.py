@@ -47,28 +47,10 @@ def parse():
 
 
 # --------------------------------------------------------------------------
-class Timer:
-    """HIP events around each kernel call, on the stream the calls use."""
-
-    def __init__(self, torch, labels):
-        self.torch = torch
-        self.labels = labels
-        self.pairs = {l: [] for l in labels}
-
-    def wrap(self, label, fn, record):
-        if not record:
-            return fn()
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
-        s.record()
-        r = fn()
-        e.record()
-        self.pairs[label].append((s, e))
-        return r
-
-    def mean_us(self, label):
-        p = self.pairs[label]
-        return 1000.0 * sum(s.elapsed_time(e) for s, e in p) / len(p) if p else None
+def fused(s):
+    """Whether csa_index_topk runs fused for shape s (one query per indexer
+    workgroup and k at most a quarter of a 2048-entry chunk)."""
+    return (s.H_I >= 64 or s.Lq == 1) and 4 * s.topk <= 2048
 
 
 def csa_decode_setup(torch, csa, wl, shape, seeds, dev):
@@ -80,24 +62,15 @@ def csa_decode_setup(torch, csa, wl, shape, seeds, dev):
         x["idx"] = torch.empty((B, Lq, shape.topk), dtype=torch.int32, device=dev)
         tb = csa.topk_ws_bytes(B, Lq, shape.q_pos0, shape.m, shape.topk)
         x["topk_ws"] = torch.empty((tb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        if fused(shape):
+            cb = csa.index_candidates_bytes(B, Lq, shape.q_pos0, shape.m, shape.topk)
+            x["cand"] = torch.empty((cb + 15) // 16 * 4, dtype=torch.float32, device=dev)
         nb = csa.sparse_attn_ws_bytes(B, Lq, shape.H, shape.D, shape.topk, shape.W)
         x["ws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
         x["out"] = torch.empty_like(x["q"])
         x["lse"] = torch.empty((B, Lq, shape.H), dtype=torch.float32, device=dev)
         sets.append(x)
     return sets
-
-
-def csa_step(csa, shape, x, tm, record, prefix=""):
-    s = shape
-    tm.wrap(prefix + "index_qk", lambda: csa.index_scores(
-        x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
-        out=x["scores"]), record)
-    tm.wrap(prefix + "topk", lambda: csa.topk(x["scores"], s.topk, s.q_pos0, s.m, out=x["idx"],
-                                              ws=x["topk_ws"]), record)
-    tm.wrap(prefix + "sparse_attn", lambda: csa.sparse_attn(
-        x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"],
-        s.q_pos0, ws=x["ws"], out=x["out"], lse=x["lse"]), record)
 
 
 def hca_setup(torch, csa, wl, shape, seeds, dev):
@@ -110,13 +83,6 @@ def hca_setup(torch, csa, wl, shape, seeds, dev):
         x["lse"] = torch.empty((shape.B, shape.Lq, shape.H), dtype=torch.float32, device=dev)
         sets.append(x)
     return sets
-
-
-def hca_step(csa, shape, x, tm, record, prefix=""):
-    s = shape
-    tm.wrap(prefix + "hca_attn", lambda: csa.hca_attn(
-        x["q"], x["k_c"], x["v_c"], s.m, x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"], s.q_pos0,
-        ws=x["ws"], out=x["out"], lse=x["lse"]), record)
 
 
 # ---------------------------------------------------------- algorithmic bytes
@@ -142,6 +108,22 @@ def sparse_attn_bytes(s):
     kvb = 2 if s.kv == "bf16" else 4
     rows = s.topk + s.W
     return s.B * s.Lq * (rows * 2 * s.D * kvb + 2 * s.H * s.D * kvb + s.H * 4 + s.topk * 4)
+
+
+def index_cand_bytes(s):
+    """Fused indexer: k_I rows, q_I and head weights read once, and the
+    per-chunk candidate lists (8 bytes a slot) written once."""
+    n_last = (s.q_pos0 + s.Lq) // s.m
+    nchunks = (n_last + 2047) // 2048
+    kb = s.B * n_last * idx_row_bytes(s)
+    qb = s.B * s.Lq * s.H_I * idx_row_bytes(s)
+    return kb + qb + s.B * s.Lq * s.H_I * 4 + s.B * s.Lq * nchunks * s.topk * 8
+
+
+def topk_merge_bytes(s):
+    n_last = (s.q_pos0 + s.Lq) // s.m
+    nchunks = (n_last + 2047) // 2048
+    return s.B * s.Lq * nchunks * s.topk * 8 + s.B * s.Lq * s.topk * 4
 
 
 def topk_bytes(s):
@@ -301,11 +283,12 @@ def main():
     for prefix, s in shapes:
         if W == "indexer_fp8_prefill":
             labels += [prefix + "index_qk"]
+        elif s.H_I and fused(s):
+            labels += [prefix + "index_cand", prefix + "topk_merge", prefix + "sparse_attn"]
         elif s.H_I:
             labels += [prefix + "index_qk", prefix + "topk", prefix + "sparse_attn"]
         else:
             labels += [prefix + "hca_attn"]
-    tm = Timer(torch, labels)
 
     def launch(label, x, s):
         """One library call of the step (kernel(s) named by label)."""
@@ -313,6 +296,11 @@ def main():
         if kind == "index_qk":
             csa.index_scores(x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
                              out=x["scores"])
+        elif kind == "index_cand":
+            csa.index_candidates(x["q_i"], x["w_i"], x["k_i"], s.topk, s.q_pos0, s.m, s.idx, x["q_i_scale"],
+                                 x["k_i_scale"], cand=x["cand"])
+        elif kind == "topk_merge":
+            csa.topk_merge(x["cand"], s.B, s.Lq, s.topk, s.q_pos0, s.m, out=x["idx"])
         elif kind == "topk":
             csa.topk(x["scores"], s.topk, s.q_pos0, s.m, out=x["idx"], ws=x["topk_ws"])
         elif kind == "sparse_attn":
@@ -372,15 +360,15 @@ def main():
     value = queries / (ms / 1000.0)
     if W == "csa_decode":
         metric, unit = "CSA decode query-tok/s @128K ctx", "query-tok/s"
-        dom = "index_qk"
-        dom_bytes = index_qk_bytes(main_shape)
+        dom = "index_cand"
+        dom_bytes = index_cand_bytes(main_shape)
         roof = {"bound": "hbm", "achieved": dom_bytes / (breakdown[dom] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
         cfg = {"workload": main_shape.name, "batch": main_shape.B, "context": main_shape.q_pos0 + 1,
                "compressed_entries": main_shape.N_cap, "heads": main_shape.H, "head_dim": main_shape.D,
                "indexer": "%dx%d %s" % (main_shape.H_I, main_shape.d_I, main_shape.idx),
                "topk": main_shape.topk, "window": main_shape.W}
-        step_bytes = index_qk_bytes(main_shape) + topk_bytes(main_shape) + sparse_attn_bytes(main_shape)
+        step_bytes = index_cand_bytes(main_shape) + topk_merge_bytes(main_shape) + sparse_attn_bytes(main_shape)
     elif W == "hca_decode":
         metric, unit = "HCA decode query-tok/s @1M ctx", "query-tok/s"
         dom = "hca_attn"
@@ -416,6 +404,7 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = None
     roof["kernel"] = dom
+    roof["bytes_per_launch"] = dom_bytes
     roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
 
     result = {

@@ -111,6 +111,9 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
  *   B, Lq, q_pos0  sequences, query rows per sequence, position of row 0
  *   m              compression block of the cache being indexed (>= 1)
  *   N_cap          rows of k_i per sequence; requires n(q_pos0+Lq-1) <= N_cap
+ *                  and N_cap * G * 4 < 2^31 bytes, G = 64 / H_i query rows
+ *                  scored together (G = 1 for H_i = 128): N_cap < 2^29 for
+ *                  H_i >= 64, < 2^25 for H_i = 4
  *   H_i, d_i       indexer heads (4, 8, 16, 32, 64 or 128) and dim
  *                  (32, 64 or 128)
  *   idx_dtype      CSA_F32, CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1
@@ -122,8 +125,14 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
  *   topk           1..2048
  *   idx_out        [B, Lq, topk] int32
  *   ws, ws_bytes   workspace of csa_index_topk_ws_bytes(B, Lq, q_pos0, m,
- *                  N_cap, topk) bytes. After the call its first B*Lq*N_cap
- *                  floats hold I[b, t, j] for the visible j (others unspecified).
+ *                  N_cap, topk) bytes; needs no initial contents, and its
+ *                  contents after the call are unspecified (the scores
+ *                  themselves are what csa_index_scores returns).
+ *
+ * When every indexer workgroup scores a single query (H_i >= 64, or Lq = 1)
+ * and 4*topk <= 2048, the top-k runs fused: each workgroup keeps the top k of
+ * its 2048-entry chunk in LDS and only those candidates reach HBM, to be
+ * merged per query; the result is the same.
  */
 size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk);
 int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
@@ -152,11 +161,41 @@ int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
  *              only, and those values must be finite.
  *   idx_out    [B, Lq, topk] int32
  *   ws, ws_bytes  workspace of csa_topk_ws_bytes(B, Lq, q_pos0, m, topk) bytes
- *              (candidate lists of rows longer than 8192 entries).
+ *              (candidate lists of rows longer than 32768 entries).
  */
 size_t csa_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int topk);
 int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores,
              int topk, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa_index_candidates, csa_topk_merge — the two launches of csa_index_topk
+ * when it runs fused, callable alone; in sequence they return what
+ * csa_index_topk returns.
+ *
+ * csa_index_candidates: the indexer of csa_index_topk with the top k of each
+ * 2048-entry chunk of a row kept on chip. For every query row (b, i) and
+ * chunk c < ceil(n(q_pos0+Lq-1) / 2048) it writes a list of topk pairs: keys
+ * (uint32, order-preserving images of the scores: a larger score has a
+ * larger key, -0 and +0 share one) at cand[(((b*Lq + i) * nc + c) * topk]
+ * and the entry indices at the same offset past the rows * nc * topk keys,
+ * in ascending index, padded with key 0 / index -1. Arguments and limits of
+ * csa_index_topk, plus H_i >= 64 or Lq == 1, and 4*topk <= 2048
+ * (else CSA_ERR_SHAPE).
+ * csa_topk_merge: the top k of each row's lists by (key descending, index
+ * ascending) into idx_out [B, Lq, topk] int32, ascending index, -1 padding.
+ * The rest of `cand` past the lists is its scratch.
+ *
+ *   cand, cand_bytes  csa_index_candidates_bytes(B, Lq, q_pos0, m, topk) bytes,
+ *                     no initial contents needed
+ */
+size_t csa_index_candidates_bytes(int B, int Lq, int64_t q_pos0, int m, int topk);
+int csa_index_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
+                         int H_i, int d_i, int idx_dtype,
+                         const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                         const void* k_i, const uint8_t* k_i_scale,
+                         int topk, void* cand, size_t cand_bytes, void* stream);
+int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, size_t cand_bytes,
+                   int32_t* idx_out, void* stream);
 
 /*
  * csa_sparse_attn — CSA attention over the selected compressed entries plus

@@ -28,6 +28,9 @@ SIGNATURES = {
     "csa_index_topk": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
     "csa_index_scores": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "csa_topk": (_I, [_I, _I, _L, _I, _L, _P, _I, _P, _P, _Z, _P]),
+    "csa_index_candidates_bytes": (_Z, [_I, _I, _L, _I, _I]),
+    "csa_index_candidates": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
+    "csa_topk_merge": (_I, [_I, _I, _L, _I, _I, _P, _Z, _P, _P]),
     "csa_sparse_attn_ws_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
                              _P, _P, _P, _P, _Z, _P]),
@@ -114,8 +117,7 @@ def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, 
 
     q_i [B, Lq, H_i, d_i] (fp4: [..., d_i/2] bytes + q_scale [..., d_i/32]),
     w_i [B, Lq, H_i] f32, k_i [B, N_cap, d_i] (fp4: bytes + k_scale).
-    fmt: 'f32' | 'bf16' | 'fp8' | 'fp4'. Returns idx [B, Lq, topk] int32; the
-    f32 scores are left in ws[: B*Lq*N_cap].
+    fmt: 'f32' | 'bf16' | 'fp8' | 'fp4'. Returns idx [B, Lq, topk] int32.
     """
     B, Lq, H_i = w_i.shape
     N_cap = k_i.shape[1]
@@ -127,6 +129,34 @@ def index_topk(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, 
     _check(lib().csa_index_topk(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
                                 _ptr(q_scale), _ptr(w_i), _ptr(k_i), _ptr(k_scale), topk, _ptr(out),
                                 _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def index_candidates_bytes(B, Lq, q_pos0, m, topk):
+    return lib().csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)
+
+
+def index_candidates(q_i, w_i, k_i, topk, q_pos0, m, fmt, q_scale=None, k_scale=None, cand=None):
+    """First launch of the fused index_topk: per-(row, 2048-entry chunk) top-k
+    candidate lists, written into (and returned as) the buffer `cand`."""
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if cand is None:
+        cand = _ws(index_candidates_bytes(B, Lq, q_pos0, m, topk), q_i.device)
+    _check(lib().csa_index_candidates(B, Lq, q_pos0, m, N_cap, H_i, d_i, IDX_FORMATS[fmt], _ptr(q_i),
+                                      _ptr(q_scale), _ptr(w_i), _ptr(k_i), _ptr(k_scale), topk, _ptr(cand),
+                                      cand.numel() * cand.element_size(), _stream()))
+    return cand
+
+
+def topk_merge(cand, B, Lq, topk, q_pos0, m, out=None):
+    """Second launch of the fused index_topk: idx [B, Lq, topk] int32 from the
+    candidate lists in `cand`."""
+    if out is None:
+        out = torch.empty((B, Lq, topk), dtype=torch.int32, device=cand.device)
+    _check(lib().csa_topk_merge(B, Lq, q_pos0, m, topk, _ptr(cand), cand.numel() * cand.element_size(),
+                                _ptr(out), _stream()))
     return out
 
 

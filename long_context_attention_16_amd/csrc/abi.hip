@@ -79,9 +79,33 @@ static size_t scores_bytes(int B, int Lq, int64_t N_cap) {
   return ((size_t)B * Lq * N_cap * sizeof(float) + 255) / 256 * 256;
 }
 
+// Fused indexer + per-chunk top-k: candidate lists of the chunks of kIdxColsPerWG
+// entries, merged by the top-k merge levels.
+static size_t fused_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
+  return topk_merge_ws_bytes((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk);
+}
+
+// The indexer's top-k runs fused when every indexer workgroup scores one query
+// (H_i >= 64, or a single query row) and k keeps at most a quarter of a chunk.
+static bool use_fused(int Lq, int H_i, int topk) {
+  return (index_qk_queries_per_group(H_i) == 1 || Lq == 1) && 4 * topk <= index_qk_list_len();
+}
+
+static int launch_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                             int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                             const void* k_i, const uint8_t* k_i_scale, int topk, void* cand, hipStream_t st) {
+  const int64_t rows = (int64_t)B * Lq;
+  uint32_t* ck = (uint32_t*)cand;
+  int32_t* ci = (int32_t*)(ck + rows * index_qk_nchunks(q_pos0, Lq, m) * topk);
+  return launch_index_qk_fused(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
+                               topk, ck, ci, st);
+}
+
 size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
   if (B <= 0 || Lq <= 0 || N_cap <= 0) return 16;
-  return scores_bytes(B, Lq, N_cap) + csa_topk_ws_bytes(B, Lq, q_pos0, m, topk);
+  const size_t unfused = scores_bytes(B, Lq, N_cap) + csa_topk_ws_bytes(B, Lq, q_pos0, m, topk);
+  const size_t fused = fused_bytes(B, Lq, q_pos0, m, topk);
+  return unfused > fused ? unfused : fused;
 }
 
 static int check_topk_shape(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
@@ -100,6 +124,7 @@ static int check_indexer(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, in
   if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
   if (!(H_i == 4 || H_i == 8 || H_i == 16 || H_i == 32 || H_i == 64 || H_i == 128)) return CSA_ERR_SHAPE;
   if (!(d_i == 32 || d_i == 64 || d_i == 128)) return CSA_ERR_SHAPE;
+  if ((int64_t)index_qk_queries_per_group(H_i) * N_cap * 4 >= 0x7FFFFFF0LL) return CSA_ERR_SHAPE;
   if (!aligned16(q_i) || !aligned16(w_i) || !aligned16(k_i)) return CSA_ERR_ALIGN;
   return CSA_OK;
 }
@@ -128,6 +153,13 @@ int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i,
   if (!ws || ws_bytes < csa_index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
   hipStream_t st = as_stream(stream);
+  if (use_fused(Lq, H_i, topk)) {
+    if (launch_candidates(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
+                          topk, ws, st))
+      return CSA_ERR_LAUNCH;
+    return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, ws, idx_out, st)
+               ? CSA_ERR_LAUNCH : CSA_OK;
+  }
   float* scores = (float*)ws;
   void* cand = (char*)ws + scores_bytes(B, Lq, N_cap);
   if (launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
@@ -144,6 +176,39 @@ int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* s
   if (!ws || ws_bytes < csa_topk_ws_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
   return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, ws, as_stream(stream))
              ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+size_t csa_index_candidates_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
+  if (B <= 0 || Lq <= 0 || m < 1 || q_pos0 < 0 || topk < 1) return 16;
+  const size_t b = fused_bytes(B, Lq, q_pos0, m, topk);
+  return b < 16 ? 16 : b;
+}
+
+int csa_index_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int idx_dtype,
+                         const void* q_i, const uint8_t* q_i_scale, const float* w_i, const void* k_i,
+                         const uint8_t* k_i_scale, int topk, void* cand, size_t cand_bytes, void* stream) {
+  if (!cand) return CSA_ERR_NULL;
+  if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                             k_i_scale, topk))
+    return rc;
+  if (!use_fused(Lq, H_i, topk)) return CSA_ERR_SHAPE;
+  if (!aligned16(cand)) return CSA_ERR_ALIGN;
+  if (cand_bytes < csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
+  if ((int64_t)B * Lq == 0) return CSA_OK;
+  return launch_candidates(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale, topk,
+                           cand, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, size_t cand_bytes,
+                   int32_t* idx_out, void* stream) {
+  if (!cand || !idx_out) return CSA_ERR_NULL;
+  if (B < 0 || Lq < 0 || q_pos0 < 0 || m < 1 || topk < 1 || topk > 2048) return CSA_ERR_SHAPE;
+  if (4 * topk > index_qk_list_len()) return CSA_ERR_SHAPE;
+  if (!aligned16(cand) || !aligned16(idx_out)) return CSA_ERR_ALIGN;
+  if (cand_bytes < csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
+  if ((int64_t)B * Lq == 0) return CSA_OK;
+  return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, cand, idx_out,
+                           as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 static int check_attn_common(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,

@@ -49,6 +49,23 @@ __host__ __device__ inline int attn_nsplit(int S) {
 int launch_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
                     const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
                     hipStream_t stream);
+// Query rows scored together by one indexer workgroup (64 / H_i, 1 for H_i = 128).
+int index_qk_queries_per_group(int H_i);
+// Entries per indexer workgroup (the length of a fused candidate source chunk)
+// and the number of such chunks per row.
+int index_qk_list_len();
+int index_qk_nchunks(int64_t q_pos0, int Lq, int m);
+// Indexer with the per-chunk top-k fused in (groups of one query only): for
+// each (row, chunk) a list of topk (key, index) pairs at
+// cand_{key,idx}[(row * nchunks + chunk) * topk].
+int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
+                          const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
+                          const uint8_t* k_s, int topk, uint32_t* cand_key, int32_t* cand_idx,
+                          hipStream_t stream);
+// Merge levels over nlists candidate lists of topk per row (rows = B * Lq),
+// then the final indices; ws holds the lists at level 0 and room for level 1.
+int launch_topk_merge(int64_t rows, int nlists, int topk, void* lists, int32_t* idx_out, hipStream_t stream);
+size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk);
 int launch_index_qk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
                     const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
                     const uint8_t* k_s, float* scores, hipStream_t stream);

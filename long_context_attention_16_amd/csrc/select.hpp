@@ -1,0 +1,176 @@
+// Workgroup-wide radix select of the k largest 32-bit keys (the top-k rule
+// of the indexer: key order first, then position). Shared by the top-k
+// kernels and the indexer's fused per-chunk selection.
+//
+// Keys live in registers, KPT per thread, key[u] of thread t at position
+// THREADS*u + t. A radix select on 11-, 11- and 10-bit digits counts into an
+// LDS histogram (each thread owns kTopkBins / THREADS bins for the search);
+// every prefix sum is a ballot-built wave scan plus one LDS exchange of wave
+// totals. Compaction counts, per (row u, wave), the equal and the selected
+// keys with ballots and scans those counts once each, so every selected
+// position gets its output slot in ascending order with no sort.
+#pragma once
+#include "common.hpp"
+
+namespace csa {
+
+constexpr int kTopkBins = 2048;
+
+template <int THREADS, int KPT> struct TopkShared {
+  int hist[kTopkBins];
+  int wtot[2][THREADS / kWave];
+  int cnt[KPT * (THREADS / kWave)];  // per (row, wave) counts, scanned in place
+  uint32_t sel_digit;
+  int sel_above;
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive scan over the workgroup of v in [0, 2^BITS); *total gets the sum.
+// Every thread calls it in the same order; `par` (a register) alternates the
+// LDS buffer of wave totals, so one barrier per scan suffices.
+template <int THREADS, int KPT, int BITS>
+__device__ __forceinline__ int block_scan(int v, int* total, TopkShared<THREADS, KPT>& S, int& par) {
+  constexpr int NW = THREADS / kWave;
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int pre = 0, wt = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    pre += lanes_below(m) << b;
+    wt += __popcll(m) << b;
+  }
+  const int buf = par;
+  par ^= 1;
+  if (lane == 0) S.wtot[buf][w] = wt;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int x = S.wtot[buf][i];
+    off += i < w ? x : 0;
+    tot += x;
+  }
+  *total = tot;
+  return off + pre;
+}
+
+// One radix pass over the register keys: count digit (key >> shift) & dmask of
+// valid keys whose higher bits equal `prefix` (under `pmask`); find the digit
+// holding the kr-th largest. Returns it; *above = counted keys in higher digits.
+// Thread t owns the BPT consecutive bins just below nb - BPT*t (nb = dmask + 1).
+template <int THREADS, int KPT>
+__device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t pmask,
+                                               int shift, uint32_t dmask, int kr, TopkShared<THREADS, KPT>& S,
+                                               int& par, int* above) {
+  constexpr int BPT = kTopkBins / THREADS;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) S.hist[tid + q * THREADS] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (u * THREADS + tid < n && (key[u] & pmask) == prefix) atomicAdd(&S.hist[(key[u] >> shift) & dmask], 1);
+  __syncthreads();
+  const int nb = (int)dmask + 1;
+  const int top = nb - 1 - BPT * tid;  // this thread's highest bin; bins top, top-1, ... top-BPT+1
+  int h[BPT], sum = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    h[q] = top - q >= 0 ? S.hist[top - q] : 0;
+    sum += h[q];
+  }
+  int tot;
+  const int ab = block_scan<THREADS, KPT, 16>(sum, &tot, S, par);
+  if (top >= 0 && ab < kr && ab + sum >= kr) {
+    int acc = ab;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (acc < kr && acc + h[q] >= kr) {
+        S.sel_digit = (uint32_t)(top - q);
+        S.sel_above = acc;
+      }
+      acc += h[q];
+    }
+  }
+  __syncthreads();
+  *above = S.sel_above;
+  return S.sel_digit;
+}
+
+// Top k (k < n <= THREADS*KPT) of the register keys, key[u] of thread t being
+// position THREADS*u + t; emit(slot, u) on the threads whose key[u] is
+// selected, slots ascending with position.
+template <int THREADS, int KPT, class Emit>
+__device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, int k, TopkShared<THREADS, KPT>& S,
+                                             const Emit& emit) {
+  constexpr int NW = THREADS / kWave;
+  constexpr int NC = KPT * NW;  // (row, wave) count cells, each at most 64
+  static_assert(NC <= THREADS, "one scan pass over the count cells");
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
+  int par = 0, above;
+  const uint32_t d0 = radix_pass<THREADS, KPT>(key, n, 0u, 0u, 21, 0x7FFu, k, S, par, &above);
+  int kr = k - above;
+  const uint32_t d1 = radix_pass<THREADS, KPT>(key, n, d0 << 21, 0x7FFu << 21, 10, 0x7FFu, kr, S, par, &above);
+  kr -= above;
+  const uint32_t pre = (d0 << 21) | (d1 << 10);
+  const uint32_t d2 = radix_pass<THREADS, KPT>(key, n, pre, 0xFFFFFC00u, 0, 0x3FFu, kr, S, par, &above);
+  const int need_eq = kr - above;
+  const uint32_t T = pre | d2;
+  const bool all_eq = need_eq == S.hist[d2];  // every key equal to T is taken: no ranks needed
+
+  int tot;
+  static_assert(KPT <= 32, "selection bits of a thread fit one word");
+  uint32_t take = 0;  // bit u: key[u] is selected
+  if (all_eq) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) take |= (uint32_t)(u * THREADS + tid < n && key[u] >= T) << u;
+  } else {
+    // ranks of the keys equal to T, in position order (row-major over (u, wave, lane))
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const uint64_t me = __ballot(u * THREADS + tid < n && key[u] == T);
+      if (lane == 0) S.cnt[u * NW + w] = __popcll(me);
+    }
+    __syncthreads();
+    {
+      const int c = tid < NC ? S.cnt[tid] : 0;
+      const int off = block_scan<THREADS, KPT, 7>(c, &tot, S, par);
+      __syncthreads();
+      if (tid < NC) S.cnt[tid] = off;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const bool ok = u * THREADS + tid < n;
+      const bool e = ok && key[u] == T;
+      const uint64_t me = __ballot(e);
+      const bool sel = (ok && key[u] > T) || (e && S.cnt[u * NW + w] + lanes_below(me) < need_eq);
+      take |= (uint32_t)sel << u;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const uint64_t ms = __ballot((take >> u) & 1);
+    if (lane == 0) S.cnt[u * NW + w] = __popcll(ms);
+  }
+  __syncthreads();
+  {
+    const int c = tid < NC ? S.cnt[tid] : 0;
+    const int off = block_scan<THREADS, KPT, 7>(c, &tot, S, par);
+    __syncthreads();
+    if (tid < NC) S.cnt[tid] = off;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
+    const bool sel = (take >> u) & 1;
+    const uint64_t ms = __ballot(sel);
+    if (sel) emit(S.cnt[u * NW + w] + lanes_below(ms), u);
+  }
+}
+
+}  // namespace csa

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 15, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -55,6 +55,10 @@ def test_ws_queries(lib):
     # one split needs no partials
     assert lib.csa_sparse_attn_ws_bytes(1, 1, 4, 128, 16, 16) == 16
     assert lib.hca_dense_attn_ws_bytes(16, 1, 1048575, 128, 64, 512, 128) > 0
+    # fused decode lists: 16 chunks of 2048 per row, k = 512, plus one merged list per row
+    assert lib.csa_index_candidates_bytes(32, 1, 131071, 4, 512) == 32 * 512 * 8 * (16 + 1)
+    # and csa_index_topk's workspace covers both of its paths
+    assert lib.csa_index_topk_ws_bytes(32, 1, 131071, 4, 32768, 512) >= 32 * 512 * 8 * (16 + 1)
 
 
 def test_compress_rejects(lib):
@@ -95,6 +99,21 @@ def test_index_topk_rejects(lib):
     assert f(*bad) == WS
     assert lib.csa_topk(1, 4, 200, 4, 64, P, 3000, P, P, 16, None) == SHAPE
     assert lib.csa_topk(1, 4, 200, 4, 64, P, 16, P, None, 16, None) == WS
+    c = lib.csa_index_candidates
+    nc = lib.csa_index_candidates_bytes(1, 4, 200, 4, 8)
+    cb = [1, 4, 200, 4, 64, 64, 128, 1, P, None, P, P, None, 8, P, nc, None]
+    bad = list(cb); bad[5] = 32
+    assert c(*bad) == SHAPE                       # 32 heads, 4 query rows: no fused path
+    bad = list(cb); bad[13] = 600
+    assert c(*bad) == SHAPE                       # k above a quarter of a 2048-entry chunk
+    bad = list(cb); bad[15] = nc - 4
+    assert c(*bad) == WS
+    bad = list(cb); bad[14] = None
+    assert c(*bad) == NULL
+    mg = lib.csa_topk_merge
+    assert mg(1, 4, 200, 4, 8, P, nc, None, None) == NULL
+    assert mg(1, 4, 200, 4, 600, P, nc, P, None) == SHAPE
+    assert mg(1, 4, 200, 4, 8, P, nc - 4, P, None) == WS
     g = lib.csa_index_scores
     sb = [1, 4, 200, 4, 64, 4, 32, 1, P, None, P, P, None, P, None]
     assert g(*sb[:13], None, None) == NULL

@@ -55,8 +55,9 @@ def _run_csa(s, x):
                          x["q_i_scale"], x["k_i_scale"], ws=ws)
     out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], idx, x["k_raw"], x["v_raw"], s.raw_pos0, s.W,
                                x["sink"], s.q_pos0)
+    scores = csa.index_scores(x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"])
     torch.cuda.synchronize()
-    return ws[:s.B * s.Lq * s.N_cap].view(s.B, s.Lq, s.N_cap), idx, out, lse
+    return scores, idx, out, lse
 
 
 def _check_csa_rows(s, x, scores, idx, out, rows, exact):

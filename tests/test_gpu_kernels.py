@@ -65,25 +65,57 @@ def _exact_indexer(B, Lq, H_i, d_i, N_cap, fmt, seed):
     return wl.indexer_inputs(s, _gen(seed), DEV)
 
 
-@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "fp4"])
-@pytest.mark.parametrize("H_i,d_i", [(4, 32), (8, 64), (16, 128), (32, 32), (64, 128), (128, 64)])
-def test_index_scores_and_topk_exact(fmt, H_i, d_i):
-    B, Lq, m, q_pos0, topk = 2, 21, 4, 4000, 100
-    N_cap = (q_pos0 + Lq) // m + 3           # 1009: ragged against 32-entry tiles
-    x = _exact_indexer(B, Lq, H_i, d_i, N_cap, fmt, seed=H_i * 7 + d_i)
-    ws = torch.zeros(csa.index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk) // 4 + 4, device=DEV)
+def _index_exact_case(fmt, H_i, d_i, B, Lq, q_pos0, m, N_cap, topk, seed):
+    x = _exact_indexer(B, Lq, H_i, d_i, N_cap, fmt, seed=seed)
+    ws = torch.empty(csa.index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk) // 4 + 4, device=DEV)
+    ws.fill_(float("nan"))                  # no initial contents are needed
     idx = csa.index_topk(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, fmt,
                          x["q_i_scale"], x["k_i_scale"], ws=ws)
+    scores = csa.index_scores(x["q_i"], x["w_i"], x["k_i"], q_pos0, m, fmt, x["q_i_scale"], x["k_i_scale"])
     torch.cuda.synchronize()
     q = dec(x["q_i"], fmt, x["q_i_scale"])
     k = dec(x["k_i"], fmt, x["k_i_scale"])
     w = dec(x["w_i"], "f32")
     want = oidx.index_scores_batch(q, w, k, q_pos0, m)
-    got = ws[:B * Lq * N_cap].view(B, Lq, N_cap).cpu().numpy().astype(np.float64)
+    got = scores.cpu().numpy().astype(np.float64)
     vis = np.isfinite(want)
     assert np.array_equal(got[vis], want[vis]), "indexer scores not exact"
+    assert np.all(np.isneginf(got[~vis])), "invisible entries written"
     want_idx = otopk.topk_batch(want, topk, q_pos0, m)
     assert np.array_equal(idx.cpu().numpy(), want_idx), "top-k indices differ"
+    if (H_i >= 64 or Lq == 1) and 4 * topk <= 2048:
+        # the fused path's two launches, called alone, give the same indices
+        cand = csa.index_candidates(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, fmt,
+                                    x["q_i_scale"], x["k_i_scale"])
+        idx2 = csa.topk_merge(cand, B, Lq, topk, q_pos0, m)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("H_i,d_i", [(4, 32), (8, 64), (16, 128), (32, 32), (64, 128), (128, 64)])
+def test_index_scores_and_topk_exact(fmt, H_i, d_i):
+    # 21 query rows: H_i >= 64 takes the fused per-chunk top-k, smaller H_i the score path
+    B, Lq, m, q_pos0, topk = 2, 21, 4, 4000, 100
+    N_cap = (q_pos0 + Lq) // m + 3           # 1009: ragged against 32-entry tiles
+    _index_exact_case(fmt, H_i, d_i, B, Lq, q_pos0, m, N_cap, topk, seed=H_i * 7 + d_i)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("H_i,d_i", [(4, 32), (16, 128), (64, 128), (128, 128)])
+def test_index_topk_decode_fused_exact(fmt, H_i, d_i):
+    # one query row: every head layout runs fused; 3 chunks of 2048 (the last ragged), heavy ties
+    B, Lq, m, topk = 3, 1, 4, 300
+    q_pos0 = 4 * 5001 - 1                    # n = 5001
+    _index_exact_case(fmt, H_i, d_i, B, Lq, q_pos0, m, 5001 + 7, topk, seed=H_i + d_i)
+
+
+@pytest.mark.parametrize("n,topk", [(700, 512), (2048, 512), (2049, 512), (4100, 1), (300, 300), (299, 300)])
+def test_index_topk_fused_edges(n, topk):
+    # chunk lists shorter than k (padding), n exactly at chunk ends, k = 1, n <= k (all selected + -1)
+    B, Lq, m = 2, 1, 4
+    q_pos0 = 4 * n - 1
+    _index_exact_case("bf16", 64, 128, B, Lq, q_pos0, m, n + 40, topk, seed=n + topk)
 
 
 # -------------------------------------------------------------------- top-k
