@@ -1,0 +1,465 @@
+// K4 for many query heads — CSA attention in two launches with no split
+// combine, for one shared KV head of dim 512 in bf16 and H a multiple of 16
+// (the decode shape: 64 heads over k + W gathered rows).
+// Workspace: P' [rows][H][slots] bf16, chunk statistics [rows][chunks][H]
+// (max, sum) and the slots' V row offsets [rows][slots] (written by phase A).
+//
+// Source: "DeepSeek V4 重磅開源！…" (InfoQ), section 混合注意力機制 (the
+// selected compressed entries plus a sliding window over raw tokens, RoPE on
+// the last 64 dims, an attention sink). Same formula as the general kernel in
+// attn.hip: one softmax over the compressed and window rows, logits
+// <RoPE(q, t), key> / sqrt(D), the sink logit joining the denominator only.
+//
+// Why two launches: splitting a query's rows over workgroups forces every
+// split to write a partial output of H x D values (64 KB at H = 64, D = 512)
+// for a combine step, as much traffic as the rows themselves. Here
+//  * phase A, one workgroup per (query, chunk of 64 source rows), gathers the
+//    chunk's K rows into LDS, computes the logits of all H heads on MFMA and
+//    writes P' = 2^(l - m_c) in bf16 with the chunk's (m_c, sum P') per head;
+//  * phase B, one workgroup per (query, 64-wide slice of D), folds the chunk
+//    statistics and the sink into per-chunk factors 2^(m_c - M) / den,
+//    gathers the V slices of all rows (128 contiguous bytes each) and
+//    accumulates O = sum_r P_r V_r on MFMA, already normalized.
+// P' carries no more rounding than the PV product needs anyway (P enters the
+// MFMA in bf16). Every reduction runs in a fixed order, so results are
+// deterministic and independent of the batch.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int kDecD = 512;           // head dim of this path
+constexpr int kArows = 64;           // source rows per phase-A chunk
+constexpr int kAline = 1024 + 16;    // LDS bytes per K row: 260 words, 4 mod 32, so the 16-byte fragment
+                                     // reads of 8 consecutive rows hit 8 disjoint groups of 4 banks
+constexpr int kDsl = 64;             // D slice of a phase-B workgroup
+constexpr int kNsl = kDecD / kDsl;   // 8
+constexpr int kBrows = 320;          // V rows staged at once by phase B
+constexpr int kBtiles = kBrows / 32;
+constexpr float kLog2eD = 1.4426950408889634f;
+constexpr float kLn2D = 0.6931471805599453f;
+
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only
+// (not for its outstanding global loads or global-to-LDS copies, which
+// __syncthreads' fence would drain, the counter being in order), then
+// s_barrier; the memory clobber keeps the compiler from moving accesses
+// across it. Copied rows are waited for explicitly (vmcnt) where needed.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+typedef short v4i16d __attribute__((ext_vector_type(4)));
+typedef short short8d __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16d lds_v4i16d;
+
+// Source of slot sp of query row qrow: 0 = masked (reads row 0 of the
+// compressed cache, which is finite), 1 = compressed entry, 2 = window row at
+// absolute position *pos. *src = element offset of the row.
+// The idx slot of a source slot, read unconditionally (clamped into the
+// list; a list of length 0 reads the first q element instead and ignores it),
+// so the lookup is one load with no branch around it.
+__device__ __forceinline__ const int32_t* idx_slot(const AttnArgs& p, int qrow, int sp) {
+  return p.topk > 0 ? p.idx + (int64_t)qrow * p.topk + min(sp, p.topk - 1) : (const int32_t*)p.q;
+}
+
+// Source of slot sp given its idx value j (idx_slot).
+__device__ __forceinline__ int dec_source(const AttnArgs& p, int b, int64_t lo, int n_w, int sp, int32_t jv,
+                                          int64_t* src, int64_t* pos) {
+  const int64_t j = p.topk > 0 ? (int64_t)jv : -1;
+  const int w = sp - p.topk;
+  const bool comp = sp < p.topk && j >= 0 && j < p.N_cap;
+  const bool win = sp >= p.topk && w < n_w;
+  *pos = win ? lo + w : 0;
+  *src = comp ? ((int64_t)b * p.N_cap + j) * kDecD
+       : win ? ((int64_t)b * p.T_raw + (lo + w - p.raw_pos0)) * kDecD
+             : (int64_t)b * p.N_cap * kDecD;
+  return comp ? 1 : win ? 2 : 0;
+}
+
+struct DecQuery {
+  int b, n_w;
+  int64_t t, lo;
+};
+
+__device__ __forceinline__ DecQuery dec_query(const AttnArgs& p, int qrow) {
+  DecQuery d;
+  d.b = qrow / p.Lq;
+  d.t = p.q_pos0 + qrow % p.Lq;
+  d.lo = d.t - p.W + 1 > 0 ? d.t - p.W + 1 : 0;
+  d.n_w = p.W > 0 ? (int)(d.t - d.lo + 1) : 0;
+  return d;
+}
+
+// Phase A: logits of all heads against one chunk of 64 source rows.
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int nchunk, int spad,
+                                                                  uint16_t* __restrict__ pp, float* __restrict__ ml,
+                                                                  int64_t* __restrict__ rowsrc) {
+  constexpr int QS = kDecD / 32;  // k-steps of 32 dims
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[kArows * kAline];
+  __shared__ int kind[kArows];
+  __shared__ int64_t rpos[kArows];
+  __shared__ const uint8_t* rsrc[kArows];
+  __shared__ float qcos[kRopePairs], qsin[kRopePairs];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, l16 = lane % 16;
+  // All chunks of a query on one XCD (workgroups are dealt to the 8 XCDs by
+  // block index modulo 8): the query's Q rows are then read once into that
+  // XCD's L2 and hit there for its other chunks.
+  const int rows = gridDim.x / nchunk;
+  const int qrow = blockIdx.x % rows, c = blockIdx.x / rows;
+  const DecQuery dq = dec_query(p, qrow);
+  const int r0 = c * kArows;
+  const int h = wave * 16 + l16;  // H == 16 * NW
+
+  // The chunk's row sources first (one slot per thread, all lookups in
+  // flight together), then this wave's Q fragments: vector-memory operations
+  // complete in order, so the barrier below waits for the lookups alone and
+  // the Q loads overlap the row copies, which are issued once every source
+  // is known.
+  // Chunk c holds the sources r * nchunk + c (r < 64), so the window rows
+  // (the last sources) spread over all chunks and so does their RoPE work.
+  const int su = (tid % kArows) * nchunk + c;
+  // Every thread reads one idx slot and the RoPE frequency of pair tid % 32
+  // (the only pair it ever rotates), unconditionally, before the Q loads.
+  const int32_t jv = *idx_slot(p, qrow, su);
+  const double rev = kRopeRev[tid % kRopePairs];
+  const uint16_t* qb = (const uint16_t*)p.q + ((int64_t)qrow * p.H + h) * kDecD;
+  uint4 qraw[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qb + 32 * s + 8 * g);
+  int64_t src, pos;
+  const int kd = dec_source(p, dq.b, dq.lo, dq.n_w, su, jv, &src, &pos);
+  if (tid < kRopePairs) rope_cos_sin_f(dq.t, rev, &qcos[tid], &qsin[tid]);
+  if (tid < kArows) {
+    kind[tid] = kd;
+    rpos[tid] = pos;
+    rsrc[tid] = (const uint8_t*)(kd == 2 ? p.k_raw : p.k_c) + src * 2;
+  }
+  lds_barrier();
+  // K rows of the chunk straight into LDS: wave w copies rows w, w + NW, ...
+  for (int r = wave; r < kArows; r += NW)
+    __builtin_amdgcn_global_load_lds((const void*)(rsrc[r] + lane * 16),
+                                     (__attribute__((address_space(3))) void*)(Ks + r * kAline), 16, 0, 0);
+  bf16x8 qf[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    const int d0 = 32 * s + 8 * g;
+    uint4 raw = qraw[s];
+    if (d0 >= kDecD - kRopeDims) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int pr = (d0 + 2 * e - (kDecD - kRopeDims)) / 2;
+        const float x0 = bf16_bits_to_f32((uint16_t)(w[e] & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+        const float cs = qcos[pr], sn = qsin[pr];
+        o[e] = (uint32_t)f32_to_bf16_bits(x0 * cs - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * cs) << 16);
+      }
+      raw = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's K row copies have landed
+  lds_barrier();
+  // RoPE of the window rows, in LDS (pairs of the last 64 dims). Thread tid
+  // rotates pair tid % 32 of rows r0' = tid / 32, r0' + R, r0' + 2R, ...
+  // (R = threads / 32); those rows hold sources R * nchunk apart, which in
+  // the window are positions R * nchunk apart, so their angles are stepped
+  // by one complex multiply each from two evaluations.
+  {
+    constexpr int R = NW * kWave / kRopePairs;
+    const int pr = tid % kRopePairs;
+    const int64_t step = (int64_t)R * nchunk;  // position step between rows r and r + R
+    float cs = 1.f, sn = 0.f, cd = 1.f, sd = 0.f;
+    bool have = false, have_d = false;
+    for (int r = tid / kRopePairs; r < kArows; r += R) {
+      if (kind[r] != 2) { have = false; continue; }
+      if (!have) {  // first window row of this thread (or after a gap): evaluate
+        rope_cos_sin_f(rpos[r], rev, &cs, &sn);
+        if (!have_d) { rope_cos_sin_f(step, rev, &cd, &sd); have_d = true; }
+      } else {
+        const float c2 = cs * cd - sn * sd, s2 = sn * cd + cs * sd;
+        cs = c2;
+        sn = s2;
+      }
+      have = r + R < kArows && kind[r + R] == 2 && rpos[r + R] == rpos[r] + step;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(Ks + r * kAline + (kDecD - kRopeDims + 2 * pr) * 2);
+      const uint32_t v = *wp;
+      const float x0 = bf16_bits_to_f32((uint16_t)(v & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(v >> 16));
+      *wp = (uint32_t)f32_to_bf16_bits(x0 * cs - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * cs) << 16);
+    }
+  }
+  lds_barrier();
+
+  // S^T = K Q^T: four 16-row tiles; lane (head l16, g) gets rows 4g..4g+3.
+  f32x4 sacc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < QS; s0 += 4) {
+    uint4 kf[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[rt][s] = *reinterpret_cast<const uint4*>(Ks + (16 * rt + l16) * kAline + (32 * (s0 + s) + 8 * g) * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[rt][s]), qf[s0 + s],
+                                                            sacc[rt], 0, 0, 0);
+  }
+  const float cscale = kLog2eD / sqrtf((float)kDecD);
+  float x[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[rt][r] = kind[16 * rt + 4 * g + r] ? sacc[rt][r] * cscale : -INFINITY;
+      mx = fmaxf(mx, x[rt][r]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  float sum = 0.f;
+  uint16_t* prow = pp + ((int64_t)qrow * p.H + h) * spad + r0;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    float e[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      e[r] = mx == -INFINITY ? 0.f : exp2f(x[rt][r] - mx);
+      sum += e[r];
+    }
+    const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(e[0]) | ((uint32_t)f32_to_bf16_bits(e[1]) << 16);
+    const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(e[2]) | ((uint32_t)f32_to_bf16_bits(e[3]) << 16);
+    *reinterpret_cast<uint2*>(prow + 16 * rt + 4 * g) = make_uint2(lo2, hi2);
+  }
+  sum += __shfl_xor(sum, 16, kWave);
+  sum += __shfl_xor(sum, 32, kWave);
+  if (g == 0) *reinterpret_cast<float2*>(ml + (((int64_t)qrow * nchunk + c) * p.H + h) * 2) = make_float2(mx, sum);
+  // for phase B: each slot's row in elements, of the compressed cache (>= 0)
+  // or of the raw rows (one's complement)
+  if (tid < kArows) rowsrc[(int64_t)qrow * spad + r0 + tid] = kd == 2 ? ~src : src;
+}
+
+// Phase B: O[:, slice] = sum over all rows of P_r V_r[slice], with
+// P_r = P'_r * 2^(m_c - M) / den for the chunk c holding row r. Every
+// dependent lookup (chunk statistics, row sources) is made by all threads at
+// once into LDS before the copies that need them are issued.
+constexpr int kMaxChunks = (2048 + 256 + kArows - 1) / kArows;  // k <= 2048, W <= 256
+
+template <int NW>
+__global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int nchunk, int spad,
+                                                                  const uint16_t* __restrict__ pp,
+                                                                  const float* __restrict__ ml,
+                                                                  const int64_t* __restrict__ rowsrc) {
+  constexpr int H = 16 * NW;
+  constexpr int NT = NW * kWave;
+  constexpr int kFc = kBrows / kArows;  // chunks per staged block
+  constexpr int kStatIt = (kMaxChunks * H + NT - 1) / NT;
+  constexpr int kSrcIt = (kBrows + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[kBrows * kDsl * 2];
+  __shared__ float2 mls[kMaxChunks * H];
+  __shared__ const uint8_t* vsrc[kBrows];
+  __shared__ float fsc[kFc][H];
+  __shared__ float Mh[H], denh[H];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, l16 = lane % 16;
+  const int rows = gridDim.x / kNsl;  // a query's slices on one XCD, as in phase A
+  const int qrow = blockIdx.x % rows, sl = blockIdx.x / rows;
+  const DecQuery dq = dec_query(p, qrow);
+  const int h = wave * 16 + l16;
+  const uint16_t* prow = pp + ((int64_t)qrow * H + h) * spad;
+
+  // Row sources of the first block (written by phase A), the chunk
+  // statistics of the query (nchunk x H pairs) and this thread's sink logit
+  // (H = NT / 4 heads, one per thread): unconditional loads, all in flight
+  // together, each consumed at once into LDS so none is deferred to a later
+  // use.
+  const int64_t* rs = rowsrc + (int64_t)qrow * spad;
+  const uint8_t* vbase = (const uint8_t*)p.v_c + sl * kDsl * 2;
+  const uint8_t* rbase = (const uint8_t*)p.v_raw + sl * kDsl * 2;
+  auto put_sources = [&](int rb, int nrows) {
+    int64_t e[kSrcIt];
+#pragma unroll
+    for (int it = 0; it < kSrcIt; ++it) e[it] = rs[rb + min(tid + it * NT, nrows - 1)];
+#pragma unroll
+    for (int it = 0; it < kSrcIt; ++it)
+      if (tid + it * NT < nrows) vsrc[tid + it * NT] = e[it] >= 0 ? vbase + e[it] * 2 : rbase + (~e[it]) * 2;
+  };
+  const float2* mlq = reinterpret_cast<const float2*>(ml) + (int64_t)qrow * nchunk * H;
+  float2 mv[kStatIt];
+#pragma unroll
+  for (int it = 0; it < kStatIt; ++it) mv[it] = mlq[min(tid + it * NT, nchunk * H - 1)];
+  const float zraw = *(p.sink ? p.sink + tid % H : (const float*)p.q);
+  put_sources(0, min(kBrows, spad));
+#pragma unroll
+  for (int it = 0; it < kStatIt; ++it)
+    if (tid + it * NT < nchunk * H) mls[tid + it * NT] = mv[it];
+  const float z2 = p.sink ? zraw * kLog2eD : -INFINITY;
+
+  f32x4 acc[kDsl / 16];
+#pragma unroll
+  for (int dt = 0; dt < kDsl / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int rb = 0; rb < spad; rb += kBrows) {
+    const int nrows = min(kBrows, spad - rb);  // a multiple of 64
+    if (rb > 0) {
+      lds_barrier();  // every wave is done with the previous block's Vs, vsrc and fsc
+      put_sources(rb, nrows);
+    }
+    lds_barrier();  // vsrc (and, first block, mls)
+    // V slices of the block into LDS: each wave copy moves 8 rows x 128 bytes.
+    // A 128-byte row spans every bank once, so the 16-byte chunks of row r
+    // are stored XOR-swizzled (position = chunk ^ 2 (r % 4)): lane l of the
+    // copy, which lands at chunk position l % 8 of row L*8 + l/8, fetches the
+    // global chunk that belongs there.
+    for (int L = wave; L < nrows / 8; L += NW) {
+      const int r = L * 8 + lane / 8;
+      __builtin_amdgcn_global_load_lds((const void*)(vsrc[r] + (((lane % 8) ^ (2 * (r % 4))) * 16)),
+                                       (__attribute__((address_space(3))) void*)(Vs + L * 1024), 16, 0, 0);
+    }
+    if (rb == 0) {
+      // Per head (one per thread): M = max(sink, chunk maxima), den = sink
+      // term + rescaled chunk sums; LDS only, while the copies fly.
+      if (tid < H) {
+        float M = z2;
+        for (int c = 0; c < nchunk; ++c) M = fmaxf(M, mls[c * H + tid].x);
+        float den = 0.f;
+        if (M != -INFINITY) {
+          den = exp2f(z2 - M);
+          for (int c = 0; c < nchunk; ++c) {
+            const float2 v = mls[c * H + tid];
+            if (v.x != -INFINITY) den += v.y * exp2f(v.x - M);
+          }
+        }
+        Mh[tid] = M;
+        denh[tid] = den;
+      }
+      lds_barrier();  // Mh, denh
+    }
+    // Per (chunk of the block, head): the factor 2^(m_c - M) / den.
+    for (int e = tid; e < kFc * H; e += NT) {
+      const int c = e / H, hh = e % H;
+      const int cg = rb / kArows + c;
+      float f = 0.f;
+      if (cg < nchunk) {
+        const float m = mls[cg * H + hh].x;
+        if (m != -INFINITY && denh[hh] > 0.f) f = exp2f(m - Mh[hh]) / denh[hh];
+      }
+      fsc[c][hh] = f;
+    }
+    // This lane's P' fragments (rows 32t + 8g .. 32t + 8g + 7 of head h),
+    // the MFMA's B operand as they are.
+    uint4 pf[kBtiles];
+#pragma unroll
+    for (int t = 0; t < kBtiles; ++t)
+      pf[t] = *reinterpret_cast<const uint4*>(prow + rb + min(32 * t, nrows - 32) + 8 * g);
+    // Pin the fragments here: loads from read-only memory may otherwise be
+    // sunk to their uses inside the loop below, one round trip per chunk.
+#pragma unroll
+    for (int t = 0; t < kBtiles; ++t) __asm__ volatile("" : "+v"(pf[t].x), "+v"(pf[t].y), "+v"(pf[t].z), "+v"(pf[t].w));
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // Vs, fsc
+    // Each chunk (two 32-row tiles) accumulates sum_r P'_r V_r on MFMA; its
+    // factor then scales that partial once per lane (a lane's accumulators all
+    // belong to head h).
+#pragma unroll
+    for (int c = 0; c < kFc; ++c) {
+      if (64 * c >= nrows) break;
+      f32x4 part[kDsl / 16];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 2 * c + tt;
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pf[t]);
+        // V^T fragments by transposed LDS reads: lane (d = l16, g) gets rows
+        // 8g..8g+7 of column 16*dt + l16. Lane j of a 16-lane group reads 8
+        // bytes at row ra = 32t + 8g + j/4 (+4), columns 16 dt + 4 (j%4) ..+3:
+        // chunk 2 dt + (j%4)/2 of the row, swizzled as stored (ra % 4 = j/4).
+        const int ra = 32 * t + 8 * g + l16 / 4;
+        const int sw = 2 * (l16 / 4);
+#pragma unroll
+        for (int dt = 0; dt < kDsl / 16; ++dt) {
+          const int off = (((2 * dt + (l16 % 4) / 2) ^ sw) * 16) + (l16 % 2) * 8;
+          const v4i16d lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16d*)(Vs + ra * kDsl * 2 + off));
+          const v4i16d hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16d*)(Vs + (ra + 4) * kDsl * 2 + off));
+          const short8d vv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          part[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb,
+                                                              tt ? part[dt] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+      }
+      const float f = fsc[c][h];
+#pragma unroll
+      for (int dt = 0; dt < kDsl / 16; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][r] = fmaf(part[dt][r], f, acc[dt][r]);
+    }
+  }
+
+  // (lse is stored last: a store before a barrier would make the barrier wait
+  // for every outstanding copy, the counter being in order)
+  if (sl == 0 && p.lse && tid < H)
+    p.lse[(int64_t)qrow * H + tid] = Mh[tid] == -INFINITY ? -INFINITY : (Mh[tid] + log2f(denh[tid])) * kLn2D;
+  uint16_t* orow = (uint16_t*)p.out + ((int64_t)qrow * H + h) * kDecD + sl * kDsl;
+#pragma unroll
+  for (int dt = 0; dt < kDsl / 16; ++dt) {
+    const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(acc[dt][0]) | ((uint32_t)f32_to_bf16_bits(acc[dt][1]) << 16);
+    const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(acc[dt][2]) | ((uint32_t)f32_to_bf16_bits(acc[dt][3]) << 16);
+    *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * g) = make_uint2(lo2, hi2);
+  }
+}
+
+}  // namespace
+
+bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D) {
+  return !hca && kv_dtype == 1 && D == kDecD && H % 16 == 0 && H >= 16 && H <= 128;
+}
+
+int attn_decode_chunks(int topk, int W) { return (topk + W + kArows - 1) / kArows; }
+
+size_t attn_decode_ws(int B, int Lq, int H, int topk, int W) {
+  const int nc = attn_decode_chunks(topk, W);
+  const size_t rows = (size_t)B * Lq;
+  const size_t pbytes = (rows * H * nc * kArows * 2 + 255) / 256 * 256;
+  const size_t mbytes = (rows * nc * H * 2 * 4 + 255) / 256 * 256;
+  return pbytes + mbytes + rows * nc * kArows * 8;
+}
+
+int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
+  const int64_t rows = (int64_t)a.B * a.Lq;
+  if (rows == 0) return 0;
+  const int nc = attn_decode_chunks(a.topk, a.W);
+  const int spad = nc * kArows;
+  uint16_t* pp = (uint16_t*)ws;
+  float* ml = (float*)((char*)ws + ((size_t)rows * a.H * spad * 2 + 255) / 256 * 256);
+  int64_t* rowsrc = (int64_t*)((char*)ml + ((size_t)rows * nc * a.H * 8 + 255) / 256 * 256);
+  if (nc == 0) return 1;
+#define CSA_DEC(NW)                                                                                       \
+  hipLaunchKernelGGL(attn_dec_qk_kernel<NW>, dim3((unsigned)(rows * nc)), dim3(NW * kWave), 0, st, a, nc,  \
+                     spad, pp, ml, rowsrc);                                                               \
+  hipLaunchKernelGGL(attn_dec_pv_kernel<NW>, dim3((unsigned)(rows * kNsl)), dim3(NW * kWave), 0, st, a, nc, \
+                     spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc)
+  switch (a.H / 16) {
+    case 1: CSA_DEC(1); break;
+    case 2: CSA_DEC(2); break;
+    case 3: CSA_DEC(3); break;
+    case 4: CSA_DEC(4); break;
+    case 5: CSA_DEC(5); break;
+    case 6: CSA_DEC(6); break;
+    case 7: CSA_DEC(7); break;
+    default: CSA_DEC(8); break;
+  }
+#undef CSA_DEC
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // namespace csa

@@ -77,12 +77,15 @@ __constant__ const double kRopeRev[32] = {
 // cos/sin of position p times the frequency of pair i. The angle is reduced
 // to a fraction of a revolution in double (exact to ~1e-11 rad for positions
 // up to 2^20), then evaluated in float on [-pi, pi].
-__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* s) {
-  const double a = (double)p * kRopeRev[i];
+__device__ __forceinline__ void rope_cos_sin_f(int64_t p, double rev, float* c, float* s) {
+  const double a = (double)p * rev;
   const float r = (float)(a - rint(a));
   const float x = r * 6.2831853071795865f;
   *s = sinf(x);
   *c = cosf(x);
+}
+__device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* s) {
+  rope_cos_sin_f(p, kRopeRev[i], c, s);
 }
 
 // ---------------------------------------------------------------- top-k keys

@@ -66,6 +66,12 @@ int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, i
 // then the final indices; ws holds the lists at level 0 and room for level 1.
 int launch_topk_merge(int64_t rows, int nlists, int topk, void* lists, int32_t* idx_out, hipStream_t stream);
 size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk);
+// CSA attention in two launches for one bf16 KV head of dim 512 and H a
+// multiple of 16 (attn_decode.hip); ws holds the bf16 P' rows and the chunk
+// statistics, attn_decode_ws bytes.
+bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D);
+size_t attn_decode_ws(int B, int Lq, int H, int topk, int W);
+int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st);
 int launch_index_qk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
                     const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
                     const uint8_t* k_s, float* scores, hipStream_t stream);

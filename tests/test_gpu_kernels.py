@@ -227,6 +227,50 @@ def test_sparse_attn(fmt, B, Lq, H, D, k, W, sink):
     assert_close(lse.cpu().numpy(), el, 5e-3 if fmt == "bf16" else 1e-5, 1e-3, what="lse")
 
 
+@pytest.mark.parametrize("B,Lq,H,k,W,q_pos0,sink", [
+    (1, 1, 32, 1024, 128, 8000, True),     # 1152 sources: two staged V blocks
+    (2, 2, 48, 200, 128, 50, True),        # window cut at t = 50 < W, padded idx
+    (1, 2, 128, 300, 40, 5000, False),     # 128 heads, no sink
+    (3, 1, 16, 64, 0, 900, True),          # compressed only
+])
+def test_sparse_attn_many_heads(B, Lq, H, k, W, q_pos0, sink):
+    # bf16, D = 512, H a multiple of 16: the two-launch path (logits, then P V per D slice)
+    fmt, D, m = "bf16", 512, 4
+    N_cap = (q_pos0 + Lq) // m + 2
+    raw_pos0 = max(0, q_pos0 - W - 1)
+    T_raw = q_pos0 + Lq - raw_pos0 + 1
+    x = _attn_inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=H + k + W)
+    idx = _rand_idx(B, Lq, k, q_pos0, m, N_cap, seed=k + H)
+    s = x["sink"] if sink else None
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], torch.from_numpy(idx).to(DEV), x["k_raw"],
+                               x["v_raw"], raw_pos0, W, s, q_pos0)
+    torch.cuda.synchronize()
+    eo, el = _oracle_attn(x, fmt, idx, q_pos0, raw_pos0, W, s)
+    assert_close(dec(out, fmt), eo, *bars(fmt), what="out")
+    assert_close(lse.cpu().numpy(), el, 5e-3, 1e-3, what="lse")
+
+
+def test_sparse_attn_many_heads_edges():
+    """The two-launch path at t < m-1: no source at all (out 0, lse -inf), a
+    sink only (out 0, lse = sink), and a window only."""
+    fmt, B, Lq, H, D, k = "bf16", 1, 3, 16, 512, 8
+    x = _attn_inputs(fmt, B, Lq, H, D, 16, 8, seed=6)
+    idx = np.full((B, Lq, k), -1, dtype=np.int32)
+    it = torch.from_numpy(idx).to(DEV)
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], 0, 0, None, 0)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0) and torch.all(torch.isneginf(lse))
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], 0, 0, x["sink"], 0)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 0)
+    assert torch.allclose(lse[0, 0].cpu(), x["sink"].cpu())
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], 0, 5, x["sink"], 0)
+    torch.cuda.synchronize()
+    eo, el = _oracle_attn(x, fmt, idx, 0, 0, 5, x["sink"])
+    assert_close(dec(out, fmt), eo, *BAR_BF16, what="window-only")
+    assert_close(lse.cpu().numpy(), el, 5e-3, 1e-3, what="window-only lse")
+
+
 def test_sparse_attn_edges():
     """t < m-1 with no window and no sink: no source at all -> out 0, lse -inf;
     with a sink only -> out 0, lse = sink; all slots -1 -> window-only."""
