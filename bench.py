@@ -137,6 +137,39 @@ def hca_bytes(s):
     return s.B * s.Lq * ((n + s.W) * 2 * s.D * kvb + 2 * s.H * s.D * kvb + s.H * 4)
 
 
+# HBM bytes per dispatch of the dominant kernel from rocprofv3 counter runs
+# (FETCH_SIZE, then WRITE_SIZE), each scaled by what the counter reads for a
+# plain copy of known size; the summary files under profiles/ record the
+# values with a SHA-256 of the kernel's sources, and the figure is reported
+# only while those sources are unchanged.
+TRAFFIC_FILES = {("csa_decode", "index_cand"): "index_qk_fused_csa_decode_128k_b32_traffic.md"}
+
+
+def kernel_sources_sha(names):
+    """SHA-256 over the named csrc/ files, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_attention_16_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    name = TRAFFIC_FILES.get((workload, kernel))
+    if not name:
+        return None
+    try:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            fields = dict(line.strip()[2:].split(": ", 1) for line in f if line.startswith("- ") and ": " in line)
+        srcs = fields["kernel sources"].split(", ")
+        if kernel_sources_sha(srcs) != fields["sources sha256"]:
+            return None
+        return float(fields["traffic bytes per dispatch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
@@ -395,6 +428,7 @@ def main():
         metric, unit = "indexer fp8 prefill query-tok/s @64K ctx", "query-tok/s"
         dom = "index_qk"
         fl = index_qk_flops(main_shape)
+        dom_bytes = index_qk_bytes(main_shape)
         roof = {"bound": "mfma", "achieved": fl / (breakdown[dom] * 1e-6) / 1e12,
                 "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s"}
         cfg = {"workload": main_shape.name, "batch": main_shape.B, "query_chunk": main_shape.Lq,
@@ -402,7 +436,7 @@ def main():
                "indexer": "%dx%d fp8" % (main_shape.H_I, main_shape.d_I)}
         step_bytes = index_qk_bytes(main_shape)
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(W, dom)
     roof["kernel"] = dom
     roof["bytes_per_launch"] = dom_bytes
     roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
