@@ -91,6 +91,15 @@ __device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* 
 // ---------------------------------------------------------------- top-k keys
 // Order-preserving map of a finite float to uint32 (larger float -> larger
 // key); -0 and +0 map to the same key.
+// max(x, 0) as one integer max on the bit pattern: a float's sign bit makes
+// every negative value (and -0) a negative int32, so they become +0 and
+// everything else passes unchanged. fmaxf on a value the compiler cannot
+// prove quiet costs an extra canonicalizing max in IEEE mode.
+__device__ __forceinline__ float relu_bits(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, v > 0 ? v : 0);
+}
+
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7FFFFFFFu) == 0) return 0x80000000u;

@@ -299,10 +299,10 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
           const float4 w4 = s_w[mt * 8 + a4 * 2 + half];
-          float v = w4.x * fmaxf(acc[mt][a4 * 4], 0.f);
-          v = fmaf(w4.y, fmaxf(acc[mt][a4 * 4 + 1], 0.f), v);
-          v = fmaf(w4.z, fmaxf(acc[mt][a4 * 4 + 2], 0.f), v);
-          v = fmaf(w4.w, fmaxf(acc[mt][a4 * 4 + 3], 0.f), v);
+          float v = w4.x * relu_bits(acc[mt][a4 * 4]);
+          v = fmaf(w4.y, relu_bits(acc[mt][a4 * 4 + 1]), v);
+          v = fmaf(w4.z, relu_bits(acc[mt][a4 * 4 + 2]), v);
+          v = fmaf(w4.w, relu_bits(acc[mt][a4 * 4 + 3]), v);
           put(mt * 8 + a4 * 2 + half, jrel, jrel < lim[mt * 4 + a4], v);
         }
     } else {
@@ -312,10 +312,10 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
       for (int g = 0; g < MTILES * 4; ++g) {
         const int mt = g / 4, a4 = g % 4;
         const float4 w4 = s_w[mt * 8 + a4 * 2 + half];
-        run = fmaf(w4.x, fmaxf(acc[mt][a4 * 4], 0.f), run);
-        run = fmaf(w4.y, fmaxf(acc[mt][a4 * 4 + 1], 0.f), run);
-        run = fmaf(w4.z, fmaxf(acc[mt][a4 * 4 + 2], 0.f), run);
-        run = fmaf(w4.w, fmaxf(acc[mt][a4 * 4 + 3], 0.f), run);
+        run = fmaf(w4.x, relu_bits(acc[mt][a4 * 4]), run);
+        run = fmaf(w4.y, relu_bits(acc[mt][a4 * 4 + 1]), run);
+        run = fmaf(w4.z, relu_bits(acc[mt][a4 * 4 + 2]), run);
+        run = fmaf(w4.w, relu_bits(acc[mt][a4 * 4 + 3]), run);
         if ((g + 1) % gpq == 0) {
           run += __shfl_xor(run, 32, kWave);
           const int qq = g / gpq;

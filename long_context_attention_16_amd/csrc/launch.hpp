@@ -55,6 +55,11 @@ int index_qk_queries_per_group(int H_i);
 // and the number of such chunks per row.
 int index_qk_list_len();
 int index_qk_nchunks(int64_t q_pos0, int Lq, int m);
+// Many-query fp8 indexer (64 heads of dim 128, at least 16 query rows per
+// sequence): same scores as launch_index_qk.
+bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq);
+int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const void* q_i,
+                            const float* w_i, const void* k_i, float* scores, hipStream_t stream);
 // Indexer with the per-chunk top-k fused in (groups of one query only): for
 // each (row, chunk) a list of topk (key, index) pairs at
 // cand_{key,idx}[(row * nchunks + chunk) * topk].

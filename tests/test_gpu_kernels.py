@@ -118,6 +118,17 @@ def test_index_topk_fused_edges(n, topk):
     _index_exact_case("bf16", 64, 128, B, Lq, q_pos0, m, n + 40, topk, seed=n + topk)
 
 
+@pytest.mark.parametrize("B,Lq,m,q_pos0,n_extra,topk", [
+    (2, 37, 4, 4 * 9000 - 20, 6, 100),   # 3 chunks of 4096 (last ragged), last query group of 5
+    (1, 16, 2, 8191, 0, 1024),           # first query sees exactly one full chunk; N_cap = n
+    (1, 64, 4, 0, 3, 100),               # queries 0..2 see nothing, the rest at most 16 entries
+])
+def test_index_prefill_fp8_exact(B, Lq, m, q_pos0, n_extra, topk):
+    # the many-query fp8 kernel (64 heads x 128, at least 16 query rows)
+    N_cap = (q_pos0 + Lq) // m + n_extra
+    _index_exact_case("fp8", 64, 128, B, Lq, q_pos0, m, N_cap, topk, seed=Lq + m)
+
+
 # -------------------------------------------------------------------- top-k
 def _topk_case(scores, k, q_pos0, m):
     t = torch.from_numpy(scores.astype(np.float32)).to(DEV)
