@@ -31,11 +31,16 @@
 //    B-fragment reads of 16 consecutive rows at one logical chunk then cover
 //    all 64 banks once (no bank conflicts, measured);
 //  * per step a wave multiplies 32 entries (one N tile, read from LDS once)
-//    by 4 M tiles: 8 MFMA 32x32x64 fp8. The epilogue of a tile's rows can run
-//    while later tiles' MFMAs execute.
+//    by 4 M tiles: 8 MFMA 32x32x64 fp8; the next step's LDS reads are issued
+//    right after and land while this step's epilogue runs, and the block
+//    hand-over (barrier, next copy) sits between a block's last MFMAs and
+//    its last epilogue, so the pipeline never drains at block ends.
 // LDS reads, not MFMA or VALU throughput, limited the earlier one-query-per-
 // wave form (every B fragment read fed 4 MFMAs and each step needed a
-// cross-half exchange through LDS); here each read feeds 8.
+// cross-half exchange through LDS); here each read feeds 8. Measured on
+// MI355X: two waves per SIMD, each overlapping the other's MFMAs with its
+// epilogue, beat one wave per SIMD with a lagged epilogue (512 registers,
+// two accumulator sets) by about 7%.
 // Entries past a query's visible count n(t) are stored through a buffer
 // resource with an offset past its end, which the hardware drops, so no store
 // is conditional.
@@ -164,12 +169,9 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
   constexpr int kDrop = 0x7FFFFFF0;
   const int row_off = half ? (int)(N_cap * 4) : 0;
 
-  // One step = entries 32g .. 32g+31 of the chunk: B fragments (two k-steps)
-  // from the LDS block, 8 MFMAs, then ReLU + weights + sum over the lane's 64
-  // heads in four independent chains, and one store of 2 x 32 scores.
-  auto step = [&](const uint8_t* kt, int st, int g) {
+  // B fragments of step st of an LDS block (two k-steps, entries 32st..+31).
+  auto frags = [&](const uint8_t* kt, int st, i32x8 (&kf)[2]) {
     const int r = 32 * st + n32;
-    i32x8 kf[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int p0 = (4 * s + 2 * half) ^ swz(r);
@@ -177,7 +179,8 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
       const uint4 x1 = *reinterpret_cast<const uint4*>(kt + r * kPfDim + 16 * (p0 ^ 1));
       kf[s] = i32x8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
-    f32x16 acc[4];
+  };
+  auto mma = [&](const i32x8 (&kf)[2], f32x16 (&acc)[4]) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -187,6 +190,10 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
         acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][s], kf[s], acc[mt], 0, 0, 0, 127, 0,
                                                                     127);
     }
+  };
+  // ReLU + weights + sum over the lane's 64 heads in four independent
+  // chains, and one store of 2 x 32 scores (step g of the chunk).
+  auto epi = [&](const f32x16 (&acc)[4], int g) {
     float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -198,30 +205,52 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot), srsrc, off, 0, 0);
   };
 
-  // One block: wait for its copies, barrier, start the copy of the block two
-  // ahead into the buffer every wave has finished with, multiply. The issue
-  // order after block blk's copies is: the stores of block blk-2, the copies
-  // of block blk+1, the stores of block blk-1 (one store per step), so
-  // waiting down to kPfLoads + kPfStores outstanding operations covers block
-  // blk and leaves the next block in flight. Copies and waits are
-  // unconditional (past the last block the copy repeats it into the free
-  // buffer), so the compiler's own wait analysis sees the same counts on
-  // every path and adds none.
-  auto block = [&](int blk, const uint8_t* kt, uint8_t* ahead) {
-    __builtin_amdgcn_s_waitcnt(pf_vmcnt(kPfLoads + kPfStores));
-    pf_lds_barrier();  // block blk is in LDS; every wave is done with block blk-1
-    issue(min(blk + 2, nblk - 1), ahead);
+  // Step order: MFMAs of step g, LDS reads of step g+1 into the same
+  // fragment registers (the MFMAs have read them), epilogue of step g while
+  // those reads land. Between the MFMAs and the epilogue of a block's last
+  // step sits the hand-over to the next block: wait for its copies, barrier,
+  // start the copy of the block three ahead into the buffer just finished,
+  // read the next block's first fragments. The issue order after block x's
+  // copies is: 8 stores, the copies of block x+1, 8 more stores, so waiting
+  // down to kPfLoads + kPfStores outstanding operations covers block x and
+  // leaves x+1 in flight. Copies, waits and the hand-over are unconditional
+  // (past the last block the copy repeats it into a free buffer and the
+  // fragment read is unused), so the compiler's own wait analysis sees the
+  // same counts on every path and adds none.
+  i32x8 kf[2];
+  f32x16 acc[4];
+  auto block = [&](int blk, const uint8_t* kt, const uint8_t* kt_next) {
 #pragma unroll
-    for (int st = 0; st < kPfSteps; ++st) step(kt, st, blk * kPfSteps + st);
+    for (int st = 0; st < kPfSteps; ++st) {
+      mma(kf, acc);
+      if (st + 1 < kPfSteps) {
+        frags(kt, st + 1, kf);
+      } else {
+        __builtin_amdgcn_s_waitcnt(pf_vmcnt(kPfLoads + kPfStores));
+        pf_lds_barrier();  // block blk+1 is in LDS; every wave is done with block blk
+        issue(min(blk + 3, nblk - 1), const_cast<uint8_t*>(kt));
+        frags(kt_next, 0, kf);
+      }
+      // Nothing crosses these points: the reads stay right behind the MFMAs
+      // (the scheduler would sink them to the end of the epilogue and expose
+      // their latency), and the next step's MFMAs stay behind this epilogue
+      // (hoisted above it they would need a second accumulator set).
+      __builtin_amdgcn_sched_barrier(0);
+      epi(acc, blk * kPfSteps + st);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   __builtin_amdgcn_s_waitcnt(0);
+  pf_lds_barrier();  // blocks 0 and 1 are in LDS
+  issue(min(2, nblk - 1), s_k2);
+  frags(s_k0, 0, kf);
   for (int blk = 0;;) {
-    block(blk, s_k0, s_k2);
+    block(blk, s_k0, s_k1);
     if (++blk >= nblk) break;
-    block(blk, s_k1, s_k0);
+    block(blk, s_k1, s_k2);
     if (++blk >= nblk) break;
-    block(blk, s_k2, s_k1);
+    block(blk, s_k2, s_k0);
     if (++blk >= nblk) break;
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
