@@ -65,23 +65,34 @@ template <> struct Chunk<float> {
 };
 
 // LDS tile of 32 source rows: 1 KB lines (every wave load writes one line),
-// each followed by kPadB bytes so the K and V^T fragment reads spread over
-// the LDS banks.
-constexpr int kPadB = 32;
-constexpr int kLineB = 1024 + kPadB;
+// each followed by a pad so the fragment reads spread over the LDS banks. A
+// 16-byte read serves 16 lanes (256 bytes, all 64 banks) per cycle: the K
+// reads of 16 consecutive one-line rows are conflict-free with a 1040-byte
+// line (260 words, 4 banks apart), while the transposed 8-byte V reads
+// (8 rows x 4 lanes per 32 lanes) want 1056 (264 words, 8 apart).
+constexpr int kLineB = 1024 + 32;
+template <typename T, int D> constexpr int k_line() { return sizeof(T) == 2 && D == 512 ? 1024 + 16 : kLineB; }
 constexpr int kMaxSplitRows = 128;  // CSA splits: at most 96 rows (k <= 2048, W <= 1024)
 
 // LDS offset of byte `byte` of tile row r (rows longer than a line continue
 // in the next line, after the pad).
-template <int ROWB>
+template <int ROWB, int LINE = kLineB>
 __device__ __forceinline__ int lds_pos(int r, int byte) {
   const int b = r * ROWB + byte;
-  return (b >> 10) * kLineB + (b & 1023);
+  return (b >> 10) * LINE + (b & 1023);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Workgroup barrier for LDS data: waits for this wave's LDS operations only,
+// then s_barrier. __syncthreads' fence would also wait for every outstanding
+// global-to-LDS copy (the counter is in order), draining the tile prefetch;
+// copies are waited for explicitly (vmcnt) where their tile is used.
+__device__ __forceinline__ void attn_lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (gfx9 encoding; expcnt and lgkmcnt not waited).
@@ -95,24 +106,28 @@ struct SplitInfo {
 };
 
 // Source of split row sp: kind 0 = masked, 1 = compressed entry, 2 = window
-// row at absolute position *pos; *src = element offset of the row.
+// row at absolute position *pos; *src = element offset of the row. Branch
+// free (selects, and an idx slot read clamped into the split's range), so
+// the copy loops around it stay straight-line code.
 template <int D, bool HCA>
 __device__ __forceinline__ int row_source(const AttnArgs& p, const SplitInfo& si, const int* sidx, int sp,
                                           int64_t* src, int64_t* pos) {
-  *src = 0;
-  *pos = 0;
-  if (sp >= si.s1) return 0;
-  if (sp < si.n_c) {
-    const int64_t j = HCA ? (int64_t)sp : (int64_t)sidx[sp - si.s0];
-    if (j < 0 || j >= p.N_cap) return 0;
-    *src = ((int64_t)si.b * p.N_cap + j) * D;
-    return 1;
+  const bool in_split = sp < si.s1;
+  const bool comp = sp < si.n_c;
+  int64_t j = sp;
+  if constexpr (!HCA) {
+    int slot = sp - si.s0;
+    slot = slot < 0 ? 0 : (slot > kMaxSplitRows - 1 ? kMaxSplitRows - 1 : slot);
+    j = sidx[slot];
   }
-  const int w = sp - si.n_c;
-  if (w >= si.n_w) return 0;
-  *pos = si.lo + w;
-  *src = ((int64_t)si.b * p.T_raw + (*pos - p.raw_pos0)) * D;
-  return 2;
+  const bool jok = j >= 0 && j < p.N_cap;
+  const int64_t wpos = si.lo + (sp - si.n_c);
+  const bool wok = sp - si.n_c < si.n_w;
+  const int kind = !in_split ? 0 : (comp ? (jok ? 1 : 0) : (wok ? 2 : 0));
+  *src = kind == 1 ? ((int64_t)si.b * p.N_cap + j) * D
+                   : (kind == 2 ? ((int64_t)si.b * p.T_raw + (wpos - p.raw_pos0)) * D : 0);
+  *pos = kind == 2 ? wpos : 0;
+  return kind;
 }
 
 // Issue the direct-to-LDS loads of the tile starting at split row ts, and
@@ -122,33 +137,45 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& p, const SplitInfo& s
                                            uint8_t* Ks, uint8_t* Vs, int* kind_out, int64_t* pos_out) {
   constexpr int ROWB = D * (int)sizeof(T);
   constexpr int NL = 32 * ROWB / 1024;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // A fixed trip count and a scalar wave index keep the copies in
+  // straight-line code: behind per-lane branches the compiler's own wait
+  // analysis loses track of which buffer has copies in flight and drains
+  // them all before the next LDS read.
+  constexpr int PER = (NL + NW - 1) / NW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
   const uint8_t* kc = (const uint8_t*)p.k_c;
   const uint8_t* vc = (const uint8_t*)p.v_c;
   const uint8_t* kr = (const uint8_t*)p.k_raw;
   const uint8_t* vr = (const uint8_t*)p.v_raw;
 #pragma unroll
-  for (int L = wave; L < NL; L += NW) {
+  for (int u = 0; u < PER; ++u) {
+    const int L = wave + NW * u;
+    if (NL % NW != 0 && L >= NL) break;  // wave-uniform: only when waves outnumber lines
     const int byte = L * 1024 + lane * 16;
     const int r = byte / ROWB;
     const int in_row = byte % ROWB;
     int64_t src, pos;
     const int kind = row_source<D, HCA>(p, si, sidx, ts + r, &src, &pos);
-    if (in_row == 0) { kind_out[r] = kind; pos_out[r] = pos; }  // the lane holding the row start
+    // every lane of row r stores the same kind and position (no branch)
+    kind_out[r] = kind;
+    pos_out[r] = pos;
     const int64_t off = kind ? src * (int64_t)sizeof(T) + in_row : in_row;  // masked: row 0 (finite)
     const uint8_t* ks = (kind == 2 ? kr : kc) + off;
     const uint8_t* vs = (kind == 2 ? vr : vc) + off;
-    __builtin_amdgcn_global_load_lds((const void*)ks, (__attribute__((address_space(3))) void*)(Ks + L * kLineB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)ks, (__attribute__((address_space(3))) void*)(Ks + L * k_line<T, D>()), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)vs, (__attribute__((address_space(3))) void*)(Vs + L * kLineB), 16, 0, 0);
   }
 }
 
-// cos/sin of the tile's window rows (only rows of kind 2 are filled).
+// cos/sin of the tile's window rows (only rows of kind 2 are filled). A
+// thread always evaluates pair threadIdx.x % 32 (the thread count is a
+// multiple of 32), whose frequency `rev` it loaded once: a table load here,
+// in the tile loop, would be waited for with every copy issued before it.
 __device__ __forceinline__ void rope_table(const int* kind, const int64_t* pos, float (*rc)[kRopePairs + 1],
-                                           float (*rs)[kRopePairs + 1], int nt_threads) {
+                                           float (*rs)[kRopePairs + 1], int nt_threads, double rev) {
   for (int e = threadIdx.x; e < 32 * kRopePairs; e += nt_threads) {
     const int r = e / kRopePairs, pr = e % kRopePairs;
-    if (kind[r] == 2) rope_cos_sin(pos[r], pr, &rc[r][pr], &rs[r][pr]);
+    if (kind[r] == 2) rope_cos_sin_f(pos[r], rev, &rc[r][pr], &rs[r][pr]);
   }
 }
 
@@ -163,12 +190,12 @@ __device__ __forceinline__ void rope_rows_lds(uint8_t* Ks, const int* kind, floa
     const int d = D - kRopeDims + 2 * pr;
     const float c = rc[r][pr], sn = rs[r][pr];
     if constexpr (sizeof(T) == 2) {
-      uint32_t* w = reinterpret_cast<uint32_t*>(Ks + lds_pos<ROWB>(r, d * 2));
+      uint32_t* w = reinterpret_cast<uint32_t*>(Ks + lds_pos<ROWB, k_line<T, D>()>(r, d * 2));
       const uint32_t v = *w;
       const float x0 = bf16_bits_to_f32((uint16_t)(v & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(v >> 16));
       *w = (uint32_t)f32_to_bf16_bits(x0 * c - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * c) << 16);
     } else {
-      float2* w = reinterpret_cast<float2*>(Ks + lds_pos<ROWB>(r, d * 4));
+      float2* w = reinterpret_cast<float2*>(Ks + lds_pos<ROWB, k_line<T, D>()>(r, d * 4));
       const float2 v = *w;
       *w = make_float2(v.x * c - v.y * sn, v.x * sn + v.y * c);
     }
@@ -184,6 +211,98 @@ struct AttnState {
   f32x4 acc[D / 32];  // this wave's half of D
   float m_run, l_run;
 };
+
+// bf16 tile for the pair of waves that shares a group of 16 heads: each
+// wave computes S^T = K Q^T for its own 16 of the tile's 32 rows only, the
+// pair swaps its row maxima and then its probabilities (bf16, the precision
+// P enters the MFMA with anyway) through LDS, and each wave accumulates
+// O^T += V^T P^T over all 32 rows for its half of D. Each wave's l_run sums
+// its own rows; the pair adds them once at the end.
+template <int D>
+__device__ __forceinline__ void compute_tile_bf(AttnState<uint16_t, D>& st, const uint8_t* Ks, const uint8_t* Vs,
+                                                const int* kind, float cscale, int dh, float* xm_own,
+                                                const float* xm_oth, uint2* xp_own, const uint2* xp_oth) {
+  constexpr int ROWB = D * 2;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16, l16 = lane % 16;
+  const int rt = dh;  // this wave's rows 16dh .. 16dh+15
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int QN = D / 32;
+  constexpr int KB = QN < 8 ? QN : 8;  // k-steps per batch of fragment reads
+#pragma unroll
+  for (int s0 = 0; s0 < QN; s0 += KB) {
+    uint4 kf[KB];
+#pragma unroll
+    for (int s = 0; s < KB; ++s)
+      kf[s] = *reinterpret_cast<const uint4*>(Ks + lds_pos<ROWB, k_line<uint16_t, D>()>(16 * rt + l16,
+                                                                                        (32 * (s0 + s) + 8 * g) * 2));
+#pragma unroll
+    for (int s = 0; s < KB; ++s)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[s]), st.qf[s0 + s], sacc, 0, 0, 0);
+  }
+  float x[4];
+  float tm = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = kind[16 * rt + 4 * g + r] != 0;
+    x[r] = ok ? sacc[r] * cscale : -INFINITY;
+    tm = fmaxf(tm, x[r]);
+  }
+  tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+  tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+  if (g == 0) xm_own[l16] = tm;
+  attn_lds_barrier();
+  const float tmax = fmaxf(tm, xm_oth[l16]);
+  const float m_new = fmaxf(st.m_run, tmax);
+  const bool none = m_new == -INFINITY;
+  const float alpha = none ? 1.f : exp2f(st.m_run - m_new);
+  float e[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    e[r] = none ? 0.f : exp2f(x[r] - m_new);
+    psum += e[r];
+  }
+  psum += __shfl_xor(psum, 16, kWave);
+  psum += __shfl_xor(psum, 32, kWave);
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= alpha;
+  const uint2 mine = make_uint2((uint32_t)f32_to_bf16_bits(e[0]) | ((uint32_t)f32_to_bf16_bits(e[1]) << 16),
+                                (uint32_t)f32_to_bf16_bits(e[2]) | ((uint32_t)f32_to_bf16_bits(e[3]) << 16));
+  xp_own[lane] = mine;
+  attn_lds_barrier();
+  const uint2 oth = xp_oth[lane];  // the partner's lane with the same head and row offset
+  const uint2 t0 = rt == 0 ? mine : oth, t1 = rt == 0 ? oth : mine;
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(t0.x, t0.y, t1.x, t1.y));
+
+  const int dt0 = dh * (D / 32);  // first d-tile of this wave's half
+  // transposed LDS reads: lane (l16, g) gets column d of rows 4g..4g+3 and 16+4g..16+4g+3
+  const int j4 = l16 / 4, jm = l16 % 4;
+  const int off_a = lds_pos<ROWB>(4 * g + j4, jm * 8) + dt0 * 32;
+  int off_b = lds_pos<ROWB>(16 + 4 * g + j4, jm * 8) + dt0 * 32;
+  // Opaque to the compiler: folded into the first base as one large
+  // immediate, some of these reads lose their LDS alias information, and
+  // the compiler then waits for every copy in flight (the next tile's
+  // prefetch) before them.
+  __asm__ volatile("" : "+v"(off_b));
+  constexpr int DB = D / 32 < 8 ? D / 32 : 8;  // d-tiles per batch of reads
+#pragma unroll
+  for (int d0 = 0; d0 < D / 32; d0 += DB) {
+    v4i16 lo4[DB], hi4[DB];
+#pragma unroll
+    for (int q = 0; q < DB; ++q) {
+      lo4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + off_a + (d0 + q) * 32));
+      hi4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Vs + off_b + (d0 + q) * 32));
+    }
+#pragma unroll
+    for (int q = 0; q < DB; ++q) {
+      const short8_t vv = {lo4[q][0], lo4[q][1], lo4[q][2], lo4[q][3], hi4[q][0], hi4[q][1], hi4[q][2], hi4[q][3]};
+      st.acc[d0 + q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, st.acc[d0 + q], 0, 0, 0);
+    }
+  }
+}
 
 // S^T = K Q^T, online softmax, O^T += V^T P^T for one tile in LDS.
 template <typename T, int D>
@@ -204,7 +323,7 @@ __device__ __forceinline__ void compute_tile(AttnState<T, D>& st, const uint8_t*
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int s = 0; s < KB; ++s)
-          kf[rt][s] = *reinterpret_cast<const uint4*>(Ks + lds_pos<ROWB>(16 * rt + l16, (32 * (s0 + s) + 8 * g) * 2));
+          kf[rt][s] = *reinterpret_cast<const uint4*>(Ks + lds_pos<ROWB, k_line<T, D>()>(16 * rt + l16, (32 * (s0 + s) + 8 * g) * 2));
 #pragma unroll
       for (int s = 0; s < KB; ++s)
 #pragma unroll
@@ -217,7 +336,7 @@ __device__ __forceinline__ void compute_tile(AttnState<T, D>& st, const uint8_t*
     for (int u = 0; u < D / 8; ++u)
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const float2 kk = *reinterpret_cast<const float2*>(Ks + lds_pos<ROWB>(16 * rt + l16, (8 * u + 2 * g) * 4));
+        const float2 kk = *reinterpret_cast<const float2*>(Ks + lds_pos<ROWB, k_line<T, D>()>(16 * rt + l16, (8 * u + 2 * g) * 4));
         sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.x, st.qf[2 * u], sacc[rt], 0, 0, 0);
         sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk.y, st.qf[2 * u + 1], sacc[rt], 0, 0, 0);
       }
@@ -259,7 +378,12 @@ __device__ __forceinline__ void compute_tile(AttnState<T, D>& st, const uint8_t*
     // transposed LDS reads: lane (l16, g) gets column d of rows 4g..4g+3 and 16+4g..16+4g+3
     const int j4 = l16 / 4, jm = l16 % 4;
     const int off_a = lds_pos<ROWB>(4 * g + j4, jm * 8) + dt0 * 32;
-    const int off_b = lds_pos<ROWB>(16 + 4 * g + j4, jm * 8) + dt0 * 32;
+    int off_b = lds_pos<ROWB>(16 + 4 * g + j4, jm * 8) + dt0 * 32;
+    // Opaque to the compiler: folded into the first base as one large
+    // immediate, some of these reads lose their LDS alias information, and
+    // the compiler then waits for every copy in flight (the next tile's
+    // prefetch) before them.
+    __asm__ volatile("" : "+v"(off_b));
     constexpr int DB = D / 32 < 8 ? D / 32 : 8;  // d-tiles per batch of reads
 #pragma unroll
     for (int d0 = 0; d0 < D / 32; d0 += DB) {
@@ -292,7 +416,8 @@ __device__ __forceinline__ void compute_tile(AttnState<T, D>& st, const uint8_t*
 
 template <typename T, int D>
 constexpr bool attn_double_buffered(int nw) {
-  return 2 * (32 * D * (int)sizeof(T) / 1024) / nw <= 32 && 4 * (32 * D * (int)sizeof(T) / 1024) * kLineB <= 140 * 1024;
+  return 2 * (32 * D * (int)sizeof(T) / 1024) / nw <= 32 &&
+         2 * (32 * D * (int)sizeof(T) / 1024) * (k_line<T, D>() + kLineB) <= 140 * 1024;
 }
 
 template <typename T, int D, int NW, bool HCA>
@@ -304,15 +429,18 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   constexpr bool DBUF = attn_double_buffered<T, D>(NW);
   constexpr int NBUF = DBUF ? 2 : 1;
   constexpr int LOADS = 2 * NL / NW;     // vector-memory ops per wave per tile
-  __shared__ __attribute__((aligned(16))) uint8_t Ks0[NL * kLineB];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[NL * k_line<T, D>()];
   __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
-  __shared__ __attribute__((aligned(16))) uint8_t Ks1[DBUF ? NL * kLineB : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[DBUF ? NL * k_line<T, D>() : 16];
   __shared__ __attribute__((aligned(16))) uint8_t Vs1[DBUF ? NL * kLineB : 16];
   __shared__ float rc[NBUF][32][kRopePairs + 1], rs[NBUF][32][kRopePairs + 1];
   __shared__ int kind[NBUF][32];
   __shared__ int64_t rpos[NBUF][32];
   __shared__ float qcos[kRopePairs], qsin[kRopePairs];
   __shared__ int sidx[HCA ? 1 : kMaxSplitRows];
+  // bf16: the wave pairs' exchange of row maxima / final sums and of P
+  __shared__ float xch_m[BF ? NW : 1][16];
+  __shared__ uint2 xch_p[BF ? NW : 1][kWave];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -341,7 +469,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
       sidx[r] = sp < si.n_c ? p.idx[(int64_t)qrow * p.topk + sp] : -1;
     }
   }
-  if (tid < kRopePairs) rope_cos_sin(si.t, tid, &qcos[tid], &qsin[tid]);
+  const double rev = kRopeRev[tid % kRopePairs];
+  if (tid < kRopePairs) rope_cos_sin_f(si.t, rev, &qcos[tid], &qsin[tid]);
   __syncthreads();
   // wave = (head group of 16, half of D): both halves compute the same S for
   // their heads; each accumulates O for its own half of D
@@ -358,8 +487,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
 #pragma unroll
   for (int s = 0; s < QL; ++s)
     qraw[s] = *reinterpret_cast<const QRaw*>(qbase + (BF ? 32 * s + 8 * g : 8 * s + 2 * g));
-  if (ntiles > 0) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0, Ks0, Vs0, kind[0], rpos[0]);
-  if (DBUF && ntiles > 1) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32, Ks1, Vs1, kind[NBUF - 1], rpos[NBUF - 1]);
+  // Copies are issued for every tile slot of the ring, also past the split's
+  // last tile (their rows are masked: row 0, which stays cached), so every
+  // path through the loop has the same memory-counter state and the
+  // compiler's own wait analysis adds no waits.
+  issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0, Ks0, Vs0, kind[0], rpos[0]);
+  if (DBUF) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32, Ks1, Vs1, kind[NBUF - 1], rpos[NBUF - 1]);
   if constexpr (BF) {
 #pragma unroll
     for (int s = 0; s < QL; ++s) {
@@ -394,7 +527,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
       st.qf[2 * u + 1] = x.y;
     }
   }
-  __syncthreads();  // row kinds/positions of the first tiles are visible
+  attn_lds_barrier();  // row kinds/positions of the first tiles are visible
   st.m_run = -INFINITY;
   st.l_run = 0.f;
 #pragma unroll
@@ -407,22 +540,31 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
     const int ts = si.s0 + 32 * tt;
     const bool win = si.n_w > 0 && ts + 32 > si.n_c;
     // kind/rpos of this buffer were written by issue_tile before a barrier
-    if (win) rope_table(kind[bi], rpos[bi], rc[bi], rs[bi], NT);
-    if (DBUF && tt + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
+    if (win) rope_table(kind[bi], rpos[bi], rc[bi], rs[bi], NT, rev);
+    // This tile's copies: everything issued after them is the next tile's.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(DBUF ? LOADS : 0));
+    attn_lds_barrier();
     if (win) {
       rope_rows_lds<T, D>(Kb, kind[bi], rc[bi], rs[bi], NT);
-      __syncthreads();
+      attn_lds_barrier();
     }
-    compute_tile<T, D>(st, Kb, Vb, kind[bi], cscale, dh);
-    __syncthreads();
-    const int nxt = tt + NBUF;
-    if (nxt < ntiles) issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32 * nxt, Kb, Vb, kind[bi], rpos[bi]);
+    if constexpr (BF)
+      compute_tile_bf<D>(st, Kb, Vb, kind[bi], cscale, dh, xch_m[wave], xch_m[wave ^ 1], xch_p[wave],
+                         xch_p[wave ^ 1]);
+    else
+      compute_tile<T, D>(st, Kb, Vb, kind[bi], cscale, dh);
+    attn_lds_barrier();
+    issue_tile<T, D, NW, HCA>(p, si, sidx, si.s0 + 32 * (tt + NBUF), Kb, Vb, kind[bi], rpos[bi]);
   };
   for (int tt = 0; tt < ntiles; tt += NBUF) {
     step(tt, Ks0, Vs0, 0);
     if (DBUF && tt + 1 < ntiles) step(tt + 1, Ks1, Vs1, NBUF - 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+  if constexpr (BF) {  // each wave of a pair summed its own rows: add the partner's
+    if (g == 0) xch_m[wave][l16] = st.l_run;
+    attn_lds_barrier();
+    st.l_run += xch_m[wave ^ 1][l16];
   }
 
   if (!hok) return;
@@ -465,59 +607,70 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   }
 }
 
-// Merge the splits of one (query, head): fixed split order.
+// Merge the splits of one (query, head) in a fixed split order. A thread
+// owns 16 bytes of the output row (8 bf16 or 4 f32 values) and keeps all the
+// row's split statistics in registers (at most kMaxSplits: a split holds at
+// least S/16 rows), so its loads of the split partials are independent and
+// issued together rather than one dependent round trip per split.
+constexpr int kMaxSplits = 16;
+constexpr int kCombThreads = 256;
 template <typename T, int D, bool HCA>
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs p) {
-  const int qrow = blockIdx.x / p.H;
-  const int h = blockIdx.x % p.H;
-  const int i = qrow % p.Lq;
+__global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs p) {
+  constexpr int VPT = 16 / (int)sizeof(T);  // values per thread
+  constexpr int TPH = D / VPT;              // threads per (query, head)
+  constexpr int HPB = kCombThreads / TPH;   // (query, head) rows per block
+  const int64_t row = (int64_t)blockIdx.x * HPB + threadIdx.x / TPH;
+  if (row >= (int64_t)p.B * p.Lq * p.H) return;
+  const int64_t qrow = row / p.H;
+  const int h = (int)(row % p.H);
+  const int i = (int)(qrow % p.Lq);
   const int64_t t = p.q_pos0 + i;
   const int n_c = HCA ? (int)((t + 1) / p.m) : p.topk;
   const int nsplit = attn_nsplit(n_c + p.W);
   if (nsplit == 1) return;
-  const int64_t slot0 = ((int64_t)qrow * p.nsplit_max) * p.H + h;
+  const int64_t slot0 = (qrow * p.nsplit_max) * p.H + h;
   const float z2 = p.sink ? p.sink[h] * kLog2e : -INFINITY;
+  float2 ml[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    ml[s] = s < nsplit ? *reinterpret_cast<const float2*>(p.ws_ml + (slot0 + (int64_t)s * p.H) * 2)
+                       : make_float2(-INFINITY, 0.f);
+  const int d = (threadIdx.x % TPH) * VPT;
+  uint4 raw[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    raw[s] = s < nsplit ? *reinterpret_cast<const uint4*>((const T*)p.ws_o + (slot0 + (int64_t)s * p.H) * D + d)
+                        : make_uint4(0, 0, 0, 0);
   float M = z2;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p.ws_ml[(slot0 + (int64_t)s * p.H) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, ml[s].x);
   float den = 0.f;
+  float wgt[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) wgt[s] = 0.f;
   if (M != -INFINITY) {
     den = exp2f(z2 - M);
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + (slot0 + (int64_t)s * p.H) * 2);
-      den += ml.y * exp2f(ml.x - M);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      wgt[s] = ml[s].x == -INFINITY ? 0.f : exp2f(ml[s].x - M);
+      den += ml[s].y * wgt[s];
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  T* orow = (T*)p.out + ((int64_t)qrow * p.H + h) * D;
-  for (int d = threadIdx.x * 4; d < D; d += 128 * 4) {
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const int64_t slot = slot0 + (int64_t)s * p.H;
-        const float ms = p.ws_ml[slot * 2];
-        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M) * inv;
-        float4 v;
-        if constexpr (sizeof(T) == 2) {
-          const uint2 r = *reinterpret_cast<const uint2*>((const T*)p.ws_o + slot * D + d);
-          v = make_float4(bf16_bits_to_f32((uint16_t)(r.x & 0xFFFF)), bf16_bits_to_f32((uint16_t)(r.x >> 16)),
-                          bf16_bits_to_f32((uint16_t)(r.y & 0xFFFF)), bf16_bits_to_f32((uint16_t)(r.y >> 16)));
-        } else {
-          v = *reinterpret_cast<const float4*>((const float*)p.ws_o + slot * D + d);
-        }
-        o[0] = fmaf(wgt, v.x, o[0]); o[1] = fmaf(wgt, v.y, o[1]);
-        o[2] = fmaf(wgt, v.z, o[2]); o[3] = fmaf(wgt, v.w, o[3]);
-      }
-    }
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(o[0]) | ((uint32_t)f32_to_bf16_bits(o[1]) << 16);
-      const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(o[2]) | ((uint32_t)f32_to_bf16_bits(o[3]) << 16);
-      *reinterpret_cast<uint2*>(orow + d) = make_uint2(lo2, hi2);
-    } else {
-      *reinterpret_cast<float4*>(orow + d) = make_float4(o[0], o[1], o[2], o[3]);
-    }
+  float o[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) o[v] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    float x[VPT];
+    Chunk<T>::unpack(raw[s], x);
+    const float w = wgt[s] * inv;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) o[v] = fmaf(w, x[v], o[v]);
   }
-  if (p.lse && threadIdx.x == 0)
-    p.lse[(int64_t)qrow * p.H + h] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
+  *reinterpret_cast<uint4*>((T*)p.out + (qrow * p.H + h) * D + d) = Chunk<T>::pack(o);
+  if (p.lse && threadIdx.x % TPH == 0)
+    p.lse[qrow * p.H + h] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
 }
 
 template <typename T, int D, bool HCA>
@@ -531,12 +684,15 @@ static void launch_attn_t(const AttnArgs& a, hipStream_t st) {
   else CSA_ATTN_NW(16);
 #undef CSA_ATTN_NW
   if (a.nsplit_max > 1)
-    hipLaunchKernelGGL((attn_combine_kernel<T, D, HCA>), dim3((unsigned)((int64_t)a.B * a.Lq * a.H)),
-                       dim3(128), 0, st, a);
+    hipLaunchKernelGGL((attn_combine_kernel<T, D, HCA>),
+                       dim3((unsigned)(((int64_t)a.B * a.Lq * a.H * D * sizeof(T) / 16 + kCombThreads - 1) /
+                                       kCombThreads)),
+                       dim3(kCombThreads), 0, st, a);
 }
 
 int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t st) {
   if ((int64_t)a.B * a.Lq == 0) return 0;
+  if (a.nsplit_max > kMaxSplits) return 1;  // cannot happen: a split holds at least S/16 rows
 #define CSA_ATTN_D(TT, HH) \
   if (a.D == 128) launch_attn_t<TT, 128, HH>(a, st); else launch_attn_t<TT, 512, HH>(a, st)
   if (kv_dtype == 0) {
