@@ -36,7 +36,7 @@ constexpr int kAline = 1024 + 16;    // LDS bytes per K row: 260 words, 4 mod 32
                                      // reads of 8 consecutive rows hit 8 disjoint groups of 4 banks
 constexpr int kDsl = 64;             // D slice of a phase-B workgroup
 constexpr int kNsl = kDecD / kDsl;   // 8
-constexpr int kBrows = 320;          // V rows staged at once by phase B
+constexpr int kBrows = 640;          // V rows staged at once by phase B
 constexpr int kBtiles = kBrows / 32;
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLn2D = 0.6931471805599453f;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
   __shared__ float Mh[H], denh[H];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int g = lane / 16, l16 = lane % 16;
   const int rows = gridDim.x / kNsl;  // a query's slices on one XCD, as in phase A
   const int qrow = blockIdx.x % rows, sl = blockIdx.x / rows;
@@ -296,6 +296,16 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
     for (int it = 0; it < kSrcIt; ++it)
       if (tid + it * NT < nrows) vsrc[tid + it * NT] = e[it] >= 0 ? vbase + e[it] * 2 : rbase + (~e[it]) * 2;
   };
+  // This lane's P' fragments of the first block (rows 32t + 8g .. +7 of head
+  // h, the MFMA's B operand as they are): independent of everything else, so
+  // issued first and in flight with the lookups and the copies.
+  uint4 pf[kBtiles];
+  auto load_pf = [&](int rb, int nrows) {
+#pragma unroll
+    for (int t = 0; t < kBtiles; ++t)
+      pf[t] = *reinterpret_cast<const uint4*>(prow + rb + min(32 * t, nrows - 32) + 8 * g);
+  };
+  load_pf(0, min(kBrows, spad));
   const float2* mlq = reinterpret_cast<const float2*>(ml) + (int64_t)qrow * nchunk * H;
   float2 mv[kStatIt];
 #pragma unroll
@@ -323,9 +333,15 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
     // are stored XOR-swizzled (position = chunk ^ 2 (r % 4)): lane l of the
     // copy, which lands at chunk position l % 8 of row L*8 + l/8, fetches the
     // global chunk that belongs there.
-    for (int L = wave; L < nrows / 8; L += NW) {
+    // A fixed trip count (rows past nrows re-copy the last row into slots
+    // that are never read): a loop with a data-dependent count would make the
+    // compiler drain every load in flight (the P' fragments) before it.
+#pragma unroll
+    for (int u = 0; u < (kBrows / 8 + NW - 1) / NW; ++u) {
+      const int L = wave + NW * u;
+      if ((kBrows / 8) % NW != 0 && L >= kBrows / 8) break;  // wave-uniform
       const int r = L * 8 + lane / 8;
-      __builtin_amdgcn_global_load_lds((const void*)(vsrc[r] + (((lane % 8) ^ (2 * (r % 4))) * 16)),
+      __builtin_amdgcn_global_load_lds((const void*)(vsrc[min(r, nrows - 1)] + (((lane % 8) ^ (2 * (r % 4))) * 16)),
                                        (__attribute__((address_space(3))) void*)(Vs + L * 1024), 16, 0, 0);
     }
     if (rb == 0) {
@@ -358,12 +374,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
       }
       fsc[c][hh] = f;
     }
-    // This lane's P' fragments (rows 32t + 8g .. 32t + 8g + 7 of head h),
-    // the MFMA's B operand as they are.
-    uint4 pf[kBtiles];
-#pragma unroll
-    for (int t = 0; t < kBtiles; ++t)
-      pf[t] = *reinterpret_cast<const uint4*>(prow + rb + min(32 * t, nrows - 32) + 8 * g);
+    if (rb > 0) load_pf(rb, nrows);
     // Pin the fragments here: loads from read-only memory may otherwise be
     // sunk to their uses inside the loop below, one round trip per chunk.
 #pragma unroll
@@ -375,7 +386,9 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
     // belong to head h).
 #pragma unroll
     for (int c = 0; c < kFc; ++c) {
-      if (64 * c >= nrows) break;
+      // a uniform guard, not a break: the loop then unrolls fully and pf stays
+      // in registers (indexed by constants)
+      if (64 * c >= nrows) continue;
       f32x4 part[kDsl / 16];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
