@@ -22,6 +22,7 @@ template <int THREADS, int KPT> struct TopkShared {
   int cnt[KPT * (THREADS / kWave)];  // per (row, wave) counts, scanned in place
   uint32_t sel_digit;
   int sel_above;
+  int sel_count;  // keys in the selected digit's bin
 };
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -59,12 +60,14 @@ __device__ __forceinline__ int block_scan(int v, int* total, TopkShared<THREADS,
 
 // One radix pass over the register keys: count digit (key >> shift) & dmask of
 // valid keys whose higher bits equal `prefix` (under `pmask`); find the digit
-// holding the kr-th largest. Returns it; *above = counted keys in higher digits.
+// holding the kr-th largest. Returns it; *above = counted keys in higher digits,
+// *count = keys in its bin (read after the pass's last barrier; the next pass
+// writes these fields only after barriers every thread has passed).
 // Thread t owns the BPT consecutive bins just below nb - BPT*t (nb = dmask + 1).
 template <int THREADS, int KPT>
 __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t pmask,
                                                int shift, uint32_t dmask, int kr, TopkShared<THREADS, KPT>& S,
-                                               int& par, int* above) {
+                                               int& par, int* above, int* count) {
   constexpr int BPT = kTopkBins / THREADS;
   const int tid = threadIdx.x;
 #pragma unroll
@@ -91,12 +94,14 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n
       if (acc < kr && acc + h[q] >= kr) {
         S.sel_digit = (uint32_t)(top - q);
         S.sel_above = acc;
+        S.sel_count = h[q];
       }
       acc += h[q];
     }
   }
   __syncthreads();
   *above = S.sel_above;
+  *count = S.sel_count;
   return S.sel_digit;
 }
 
@@ -110,16 +115,33 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   constexpr int NC = KPT * NW;  // (row, wave) count cells, each at most 64
   static_assert(NC <= THREADS, "one scan pass over the count cells");
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
-  int par = 0, above;
-  const uint32_t d0 = radix_pass<THREADS, KPT>(key, n, 0u, 0u, 21, 0x7FFu, k, S, par, &above);
+  int par = 0, above, bc;
+  // Threshold T and whether every key equal to T is taken. A pass whose
+  // selected bin is taken whole ends the search early: the selection is then
+  // every key at or above the bin's lower bound (no ties to rank). After the
+  // second digit (22 key bits) that is the common case.
+  uint32_t T;
+  bool all_eq;
+  int need_eq = 0;
+  const uint32_t d0 = radix_pass<THREADS, KPT>(key, n, 0u, 0u, 21, 0x7FFu, k, S, par, &above, &bc);
   int kr = k - above;
-  const uint32_t d1 = radix_pass<THREADS, KPT>(key, n, d0 << 21, 0x7FFu << 21, 10, 0x7FFu, kr, S, par, &above);
-  kr -= above;
-  const uint32_t pre = (d0 << 21) | (d1 << 10);
-  const uint32_t d2 = radix_pass<THREADS, KPT>(key, n, pre, 0xFFFFFC00u, 0, 0x3FFu, kr, S, par, &above);
-  const int need_eq = kr - above;
-  const uint32_t T = pre | d2;
-  const bool all_eq = need_eq == S.hist[d2];  // every key equal to T is taken: no ranks needed
+  if (kr == bc) {
+    T = d0 << 21;
+    all_eq = true;
+  } else {
+    const uint32_t d1 = radix_pass<THREADS, KPT>(key, n, d0 << 21, 0x7FFu << 21, 10, 0x7FFu, kr, S, par, &above, &bc);
+    kr -= above;
+    const uint32_t pre = (d0 << 21) | (d1 << 10);
+    if (kr == bc) {
+      T = pre;
+      all_eq = true;
+    } else {
+      const uint32_t d2 = radix_pass<THREADS, KPT>(key, n, pre, 0xFFFFFC00u, 0, 0x3FFu, kr, S, par, &above, &bc);
+      need_eq = kr - above;
+      T = pre | d2;
+      all_eq = need_eq == bc;  // every key equal to T is taken: no ranks needed
+    }
+  }
 
   int tot;
   static_assert(KPT <= 32, "selection bits of a thread fit one word");
