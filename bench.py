@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode",
-                    choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill"])
+                    choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB copy (calibration run for HBM byte counters)")
@@ -170,6 +170,63 @@ def measured_traffic(workload, kernel):
         return None
 
 
+# Compressor workloads: (name, T tokens of one sequence, D, m); bf16 K and V.
+COMPRESS_CASES = [("ctx64k_d128_m4", 65536, 128, 4), ("seq1m_d512_m4", 1 << 20, 512, 4),
+                  ("seq1m_d512_m128", 1 << 20, 512, 128)]
+
+
+def bench_compress(args, torch, csa, dev):
+    """HBM bandwidth of csa_compress: K and V rows read once, compressed rows
+    written once (bytes = 2*T*D*2 + 2*(T/m)*D*2), timed with HIP-graph replays
+    of back-to-back calls."""
+    out = {}
+    for name, T, D, m in COMPRESS_CASES:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        k_raw = torch.randn((1, T, D), generator=gen, device=dev).to(torch.bfloat16)
+        v_raw = torch.randn((1, T, D), generator=gen, device=dev).to(torch.bfloat16)
+        w_gate = torch.randn((D,), generator=gen, device=dev) / D ** 0.5
+        k_c = torch.empty((1, T // m, D), dtype=torch.bfloat16, device=dev)
+        v_c = torch.empty_like(k_c)
+        for _ in range(max(args.warmup, 2)):
+            csa.compress(k_raw, v_raw, w_gate, m, 0, k_c, v_c)
+        torch.cuda.synchronize()
+        reps = max(args.steps // 5, 2)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                csa.compress(k_raw, v_raw, w_gate, m, 0, k_c, v_c)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / (5 * reps)
+        nbytes = 2 * T * D * 2 + 2 * (T // m) * D * 2
+        out[name] = {"us": round(us, 2), "gbs": round(nbytes / us / 1e3, 1), "bytes": nbytes}
+        del k_raw, v_raw, k_c, v_c
+        torch.cuda.empty_cache()
+    main_case = out["seq1m_d512_m4"]
+    roof = {"bound": "hbm", "achieved": main_case["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(main_case["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "compress",
+            "bytes_per_launch": main_case["bytes"]}
+    result = {
+        "metric": "compressor HBM GB/s (1M tokens, D=512, m=4)", "value": main_case["gbs"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_case["us"] / 1000.0, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) raw K/V rows)",
+        "config": {"workload": "compress_seq1m_d512_m4", "cases": {c[0]: {"tokens": c[1], "head_dim": c[2], "m": c[3]}
+                                                                  for c in COMPRESS_CASES}},
+        "roofline": roof, "cases": out,
+        "timing": "HIP-graph replays of back-to-back calls per case",
+        "copy_ceiling_gbs": copy_ceiling(torch, dev), "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
@@ -283,6 +340,9 @@ def main():
         return
 
     W = args.workload
+    if W == "compress":
+        bench_compress(args, torch, csa, dev)
+        return
     if W == "csa_decode":
         shapes = [("", wl.CFG2)]
     elif W == "hca_decode":

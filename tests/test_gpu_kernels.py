@@ -37,6 +37,10 @@ def _gen(seed):
     ("bf16", 512, 128, 2, 384, 128, 4),
     ("f32", 512, 1, 1, 37, 5, 64),
     ("bf16", 512, 4, 1, 4096, 61440, 16384),
+    # D = 128 reads four rows per wave load: m = 1, a partial last quad (m = 7), many quads (m = 128)
+    ("bf16", 128, 1, 2, 37, 5, 64),
+    ("f32", 128, 7, 1, 100, 14, 40),
+    ("bf16", 128, 128, 1, 512, 0, 8),
 ])
 def test_compress(fmt, D, m, B, T, pos0, N_cap):
     g = _gen(11)
