@@ -32,6 +32,8 @@ namespace {
 
 constexpr int kDecD = 512;           // head dim of this path
 constexpr int kArows = 64;           // source rows per phase-A chunk
+constexpr int kAtiles = kArows / 16;   // 16-row MFMA tiles of a chunk
+constexpr int kCtiles = kArows / 32;   // 32-row phase-B tiles of a chunk
 constexpr int kAline = 1024 + 16;    // LDS bytes per K row: 260 words, 4 mod 32, so the 16-byte fragment
                                      // reads of 8 consecutive rows hit 8 disjoint groups of 4 banks
 constexpr int kDsl = 64;             // D slice of a phase-B workgroup
@@ -196,30 +198,30 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int
   }
   lds_barrier();
 
-  // S^T = K Q^T: four 16-row tiles; lane (head l16, g) gets rows 4g..4g+3.
-  f32x4 sacc[4];
+  // S^T = K Q^T: kAtiles 16-row tiles; lane (head l16, g) gets rows 4g..4g+3.
+  f32x4 sacc[kAtiles];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < kAtiles; ++rt) sacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s0 = 0; s0 < QS; s0 += 4) {
-    uint4 kf[4][4];
+    uint4 kf[kAtiles][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < kAtiles; ++rt)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         kf[rt][s] = *reinterpret_cast<const uint4*>(Ks + (16 * rt + l16) * kAline + (32 * (s0 + s) + 8 * g) * 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < kAtiles; ++rt)
         sacc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[rt][s]), qf[s0 + s],
                                                             sacc[rt], 0, 0, 0);
   }
   const float cscale = kLog2eD / sqrtf((float)kDecD);
-  float x[4][4];
+  float x[kAtiles][4];
   float mx = -INFINITY;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < kAtiles; ++rt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       x[rt][r] = kind[16 * rt + 4 * g + r] ? sacc[rt][r] * cscale : -INFINITY;
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int
   float sum = 0.f;
   uint16_t* prow = pp + ((int64_t)qrow * p.H + h) * spad + r0;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < kAtiles; ++rt) {
     float e[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -388,11 +390,11 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
     for (int c = 0; c < kFc; ++c) {
       // a uniform guard, not a break: the loop then unrolls fully and pf stays
       // in registers (indexed by constants)
-      if (64 * c >= nrows) continue;
+      if (kArows * c >= nrows) continue;
       f32x4 part[kDsl / 16];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int t = 2 * c + tt;
+      for (int tt = 0; tt < kCtiles; ++tt) {
+        const int t = kCtiles * c + tt;
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pf[t]);
         // V^T fragments by transposed LDS reads: lane (d = l16, g) gets rows
         // 8g..8g+7 of column 16*dt + l16. Lane j of a 16-lane group reads 8

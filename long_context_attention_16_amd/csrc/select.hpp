@@ -18,6 +18,7 @@ constexpr int kTopkBins = 2048;
 
 template <int THREADS, int KPT> struct TopkShared {
   int hist[kTopkBins];
+  uint32_t wmin[THREADS / kWave], wmax[THREADS / kWave];
   int wtot[2][THREADS / kWave];
   int cnt[KPT * (THREADS / kWave)];  // per (row, wave) counts, scanned in place
   uint32_t sel_digit;
@@ -116,31 +117,56 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   static_assert(NC <= THREADS, "one scan pass over the count cells");
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   int par = 0, above, bc;
-  // Threshold T and whether every key equal to T is taken. A pass whose
-  // selected bin is taken whole ends the search early: the selection is then
-  // every key at or above the bin's lower bound (no ties to rank). After the
-  // second digit (22 key bits) that is the common case.
-  uint32_t T;
-  bool all_eq;
+  // Digits start below the bits every valid key shares (found from the block
+  // minimum and maximum): the top bits of scores of one magnitude are nearly
+  // constant, and a first digit taken there would pile most keys into a few
+  // histogram bins (serialized LDS atomics) and resolve little.
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int u = 0; u < KPT; ++u)
+    if (u * THREADS + tid < n) { mn = min(mn, key[u]); mx = max(mx, key[u]); }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if (lane == 0) { S.wmin[w] = mn; S.wmax[w] = mx; }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) { mn = min(mn, S.wmin[i]); mx = max(mx, S.wmax[i]); }
+  // Threshold T and whether every key equal to T is taken. Up to three
+  // digits of at most 11 bits cover the bits below the common prefix; a pass
+  // whose selected bin is taken whole ends the search early (the selection is
+  // then every key at or above the bin's lower bound, no ties to rank).
+  int rem = mn == mx ? 0 : 32 - __builtin_clz(mn ^ mx);  // bits below the common prefix
+  uint32_t pmask = rem == 32 ? 0u : ~0u << rem;
+  uint32_t prefix = mx & pmask;
+  uint32_t T = prefix;
+  bool all_eq = false, done = false;
   int need_eq = 0;
-  const uint32_t d0 = radix_pass<THREADS, KPT>(key, n, 0u, 0u, 21, 0x7FFu, k, S, par, &above, &bc);
-  int kr = k - above;
-  if (kr == bc) {
-    T = d0 << 21;
-    all_eq = true;
-  } else {
-    const uint32_t d1 = radix_pass<THREADS, KPT>(key, n, d0 << 21, 0x7FFu << 21, 10, 0x7FFu, kr, S, par, &above, &bc);
+  int kr = k;
+  bc = n;  // with no bits left (all keys equal) the bin is every key
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    if (done || rem == 0) break;
+    const int wd = rem < 11 ? rem : 11;
+    const int shift = rem - wd;
+    const uint32_t dmask = (1u << wd) - 1u;
+    const uint32_t d = radix_pass<THREADS, KPT>(key, n, prefix, pmask, shift, dmask, kr, S, par, &above, &bc);
     kr -= above;
-    const uint32_t pre = (d0 << 21) | (d1 << 10);
-    if (kr == bc) {
-      T = pre;
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    rem = shift;
+    if (kr == bc) {  // the bin is taken whole
+      T = prefix;
       all_eq = true;
-    } else {
-      const uint32_t d2 = radix_pass<THREADS, KPT>(key, n, pre, 0xFFFFFC00u, 0, 0x3FFu, kr, S, par, &above, &bc);
-      need_eq = kr - above;
-      T = pre | d2;
-      all_eq = need_eq == bc;  // every key equal to T is taken: no ranks needed
+      done = true;
     }
+  }
+  if (!done) {  // no bits left: the bin holds the single key value T
+    T = prefix;
+    need_eq = kr;
+    all_eq = kr == bc;
   }
 
   int tot;
