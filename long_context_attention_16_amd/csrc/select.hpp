@@ -3,12 +3,12 @@
 // kernels and the indexer's fused per-chunk selection.
 //
 // Keys live in registers, KPT per thread, key[u] of thread t at position
-// THREADS*u + t. A radix select on 11-, 11- and 10-bit digits counts into an
+// THREADS*u + t. A radix select on digits of at most 11 bits counts into an
 // LDS histogram (each thread owns kTopkBins / THREADS bins for the search);
-// every prefix sum is a ballot-built wave scan plus one LDS exchange of wave
-// totals. Compaction counts, per (row u, wave), the equal and the selected
-// keys with ballots and scans those counts once each, so every selected
-// position gets its output slot in ascending order with no sort.
+// every prefix sum is a DPP wave scan plus one LDS exchange of wave totals.
+// Compaction counts, per (row u, wave), the equal and the selected keys with
+// ballots and scans those counts once each, so every selected position gets
+// its output slot in ascending order with no sort.
 #pragma once
 #include "common.hpp"
 
@@ -30,20 +30,31 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exclusive scan over the workgroup of v in [0, 2^BITS); *total gets the sum.
-// Every thread calls it in the same order; `par` (a register) alternates the
-// LDS buffer of wave totals, so one barrier per scan suffices.
-template <int THREADS, int KPT, int BITS>
+// Inclusive scan over the 64 lanes of a wave with DPP moves: shifts by 1, 2,
+// 4 and 8 lanes within each row of 16, then the last lane of row 0 added to
+// row 1 and of row 2 to row 3 (row_bcast:15), then the last lane of row 1 to
+// rows 2 and 3 (row_bcast:31). Lanes whose source is outside the pattern
+// add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Exclusive scan over the workgroup of v >= 0; *total gets the sum. Every
+// thread calls it in the same order; `par` (a register) alternates the LDS
+// buffer of wave totals, so one barrier per scan suffices.
+template <int THREADS, int KPT>
 __device__ __forceinline__ int block_scan(int v, int* total, TopkShared<THREADS, KPT>& S, int& par) {
   constexpr int NW = THREADS / kWave;
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int pre = 0, wt = 0;
-#pragma unroll
-  for (int b = 0; b < BITS; ++b) {
-    const uint64_t m = __ballot((v >> b) & 1);
-    pre += lanes_below(m) << b;
-    wt += __popcll(m) << b;
-  }
+  const int inc = wave_incl_scan(v);
+  const int pre = inc - v;
+  const int wt = __builtin_amdgcn_readlane(inc, kWave - 1);
   const int buf = par;
   par ^= 1;
   if (lane == 0) S.wtot[buf][w] = wt;
@@ -59,14 +70,15 @@ __device__ __forceinline__ int block_scan(int v, int* total, TopkShared<THREADS,
   return off + pre;
 }
 
-// One radix pass over the register keys: count digit (key >> shift) & dmask of
-// valid keys whose higher bits equal `prefix` (under `pmask`); find the digit
+// One radix pass over the register keys, counted as key - base: count digit
+// (x >> shift) & dmask of valid x whose higher bits equal `prefix` (under
+// `pmask`); find the digit
 // holding the kr-th largest. Returns it; *above = counted keys in higher digits,
 // *count = keys in its bin (read after the pass's last barrier; the next pass
 // writes these fields only after barriers every thread has passed).
 // Thread t owns the BPT consecutive bins just below nb - BPT*t (nb = dmask + 1).
 template <int THREADS, int KPT>
-__device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n, uint32_t prefix, uint32_t pmask,
+__device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], uint32_t base, int n, uint32_t prefix, uint32_t pmask,
                                                int shift, uint32_t dmask, int kr, TopkShared<THREADS, KPT>& S,
                                                int& par, int* above, int* count) {
   constexpr int BPT = kTopkBins / THREADS;
@@ -76,7 +88,8 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
-    if (u * THREADS + tid < n && (key[u] & pmask) == prefix) atomicAdd(&S.hist[(key[u] >> shift) & dmask], 1);
+    if (u * THREADS + tid < n && ((key[u] - base) & pmask) == prefix)
+      atomicAdd(&S.hist[((key[u] - base) >> shift) & dmask], 1);
   __syncthreads();
   const int nb = (int)dmask + 1;
   const int top = nb - 1 - BPT * tid;  // this thread's highest bin; bins top, top-1, ... top-BPT+1
@@ -87,7 +100,7 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], int n
     sum += h[q];
   }
   int tot;
-  const int ab = block_scan<THREADS, KPT, 16>(sum, &tot, S, par);
+  const int ab = block_scan<THREADS, KPT>(sum, &tot, S, par);
   if (top >= 0 && ab < kr && ab + sum >= kr) {
     int acc = ab;
 #pragma unroll
@@ -117,10 +130,10 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   static_assert(NC <= THREADS, "one scan pass over the count cells");
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   int par = 0, above, bc;
-  // Digits start below the bits every valid key shares (found from the block
-  // minimum and maximum): the top bits of scores of one magnitude are nearly
-  // constant, and a first digit taken there would pile most keys into a few
-  // histogram bins (serialized LDS atomics) and resolve little.
+  // Keys are counted as key - min over the valid keys, and digits cover only
+  // the bits of max - min: the top bits of float keys (sign, exponent) take
+  // few values, and a first digit taken there would pile most keys into a
+  // few histogram bins (serialized LDS atomics) and resolve little.
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
@@ -135,13 +148,14 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
 #pragma unroll
   for (int i = 0; i < NW; ++i) { mn = min(mn, S.wmin[i]); mx = max(mx, S.wmax[i]); }
   // Threshold T and whether every key equal to T is taken. Up to three
-  // digits of at most 11 bits cover the bits below the common prefix; a pass
+  // digits of at most 11 bits cover the bits of max - min; a pass
   // whose selected bin is taken whole ends the search early (the selection is
   // then every key at or above the bin's lower bound, no ties to rank).
-  int rem = mn == mx ? 0 : 32 - __builtin_clz(mn ^ mx);  // bits below the common prefix
+  const uint32_t base = mn;
+  int rem = mn == mx ? 0 : 32 - __builtin_clz(mx - mn);  // digit bits left
   uint32_t pmask = rem == 32 ? 0u : ~0u << rem;
-  uint32_t prefix = mx & pmask;
-  uint32_t T = prefix;
+  uint32_t prefix = 0;  // of key - base
+  uint32_t T = base;
   bool all_eq = false, done = false;
   int need_eq = 0;
   int kr = k;
@@ -152,19 +166,19 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
     const int wd = rem < 11 ? rem : 11;
     const int shift = rem - wd;
     const uint32_t dmask = (1u << wd) - 1u;
-    const uint32_t d = radix_pass<THREADS, KPT>(key, n, prefix, pmask, shift, dmask, kr, S, par, &above, &bc);
+    const uint32_t d = radix_pass<THREADS, KPT>(key, base, n, prefix, pmask, shift, dmask, kr, S, par, &above, &bc);
     kr -= above;
     prefix |= d << shift;
     pmask |= dmask << shift;
     rem = shift;
     if (kr == bc) {  // the bin is taken whole
-      T = prefix;
+      T = base + prefix;
       all_eq = true;
       done = true;
     }
   }
   if (!done) {  // no bits left: the bin holds the single key value T
-    T = prefix;
+    T = base + prefix;
     need_eq = kr;
     all_eq = kr == bc;
   }
@@ -185,7 +199,7 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
     __syncthreads();
     {
       const int c = tid < NC ? S.cnt[tid] : 0;
-      const int off = block_scan<THREADS, KPT, 7>(c, &tot, S, par);
+      const int off = block_scan<THREADS, KPT>(c, &tot, S, par);
       __syncthreads();
       if (tid < NC) S.cnt[tid] = off;
       __syncthreads();
@@ -208,7 +222,7 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   __syncthreads();
   {
     const int c = tid < NC ? S.cnt[tid] : 0;
-    const int off = block_scan<THREADS, KPT, 7>(c, &tot, S, par);
+    const int off = block_scan<THREADS, KPT>(c, &tot, S, par);
     __syncthreads();
     if (tid < NC) S.cnt[tid] = off;
     __syncthreads();
