@@ -21,6 +21,11 @@ Readings taken here (the pages give no formula):
     denominator with a zero value; absent sink = -inf;
   * with no source and no sink the output is 0 and lse is -inf.
 
+Per-sequence positions and the state cache (see state.py): q_pos0 may be one
+position for the batch or one per sequence ([B]); query row i of sequence b
+is at q_pos0[b] + i. With ring=True the raw rows are a ring of R = T_raw
+slots, position s in slot s % R, and raw_pos0 is not used.
+
 Returned lse = M + ln(e^(z-M) + sum e^(l-M)), M = max(z, max l).
 """
 import math
@@ -58,15 +63,24 @@ def attend_one(q, t, keys, vals, win_k_raw, win_pos, win_v, sink):
     return o, lse
 
 
-def _window(t, W, raw_pos0, T_raw):
+def _window(t, W, raw_pos0, T_raw, ring=False):
+    """Absolute positions of the window of a query at t, and their raw rows."""
     lo = max(0, t - W + 1)
     pos = np.arange(lo, t + 1) if W > 0 else np.arange(0)
+    if ring:
+        assert len(pos) <= T_raw, "window longer than the ring"
+        return pos, pos % T_raw
     if len(pos):
         assert pos[0] >= raw_pos0 and pos[-1] - raw_pos0 < T_raw, "raw window not covered"
-    return pos
+    return pos, pos - raw_pos0
 
 
-def csa_sparse_attn(q, q_pos0, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink):
+def seq_pos(q_pos0, b):
+    """Position of query row 0 of sequence b (one for all, or per sequence)."""
+    return int(q_pos0) if np.ndim(q_pos0) == 0 else int(np.asarray(q_pos0)[b])
+
+
+def csa_sparse_attn(q, q_pos0, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink, ring=False):
     """CSA attention for a batch.
 
     q [B, Lq, H, D]; k_c, v_c [B, N, D]; idx [B, Lq, k] (-1 = unused slot);
@@ -81,17 +95,17 @@ def csa_sparse_attn(q, q_pos0, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink):
     T_raw = k_raw.shape[1]
     for b in range(B):
         for i in range(Lq):
-            t = q_pos0 + i
+            t = seq_pos(q_pos0, b) + i
             sel = np.asarray(idx[b, i])
             sel = sel[sel >= 0]
-            pos = _window(t, W, raw_pos0, T_raw)
+            pos, rows = _window(t, W, raw_pos0, T_raw, ring)
             out[b, i], lse[b, i] = attend_one(
                 q[b, i], t, k_c[b][sel], v_c[b][sel],
-                k_raw[b][pos - raw_pos0], pos, v_raw[b][pos - raw_pos0], sink)
+                k_raw[b][rows], pos, v_raw[b][rows], sink)
     return out, lse
 
 
-def hca_dense_attn(q, q_pos0, m, k_c, v_c, k_raw, v_raw, raw_pos0, W, sink):
+def hca_dense_attn(q, q_pos0, m, k_c, v_c, k_raw, v_raw, raw_pos0, W, sink, ring=False):
     """HCA attention for a batch: every visible compressed entry j < (t+1)//m,
     plus the window and the sink. Shapes as in csa_sparse_attn."""
     q = np.asarray(q, dtype=np.float64)
@@ -101,11 +115,11 @@ def hca_dense_attn(q, q_pos0, m, k_c, v_c, k_raw, v_raw, raw_pos0, W, sink):
     T_raw = k_raw.shape[1]
     for b in range(B):
         for i in range(Lq):
-            t = q_pos0 + i
+            t = seq_pos(q_pos0, b) + i
             n = n_visible(t, m)
             assert n <= k_c.shape[1], "compressed cache does not hold every visible entry"
-            pos = _window(t, W, raw_pos0, T_raw)
+            pos, rows = _window(t, W, raw_pos0, T_raw, ring)
             out[b, i], lse[b, i] = attend_one(
                 q[b, i], t, k_c[b][:n], v_c[b][:n],
-                k_raw[b][pos - raw_pos0], pos, v_raw[b][pos - raw_pos0], sink)
+                k_raw[b][rows], pos, v_raw[b][rows], sink)
     return out, lse

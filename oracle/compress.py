@@ -23,12 +23,16 @@ import numpy as np
 from .rope import apply_rope
 
 
-def compress(k_raw, v_raw, w_gate, m, pos0=0):
+def compress(k_raw, v_raw, w_gate, m, pos0=0, x_raw=None):
     """Compress raw rows of one sequence.
 
     k_raw, v_raw: [T, D] float64 (pre-RoPE keys, values) at absolute positions
     pos0 .. pos0+T-1. w_gate: [D]. Returns (k_c, v_c), each [T // m, D]; row i
     is the block whose absolute index is pos0 // m + i.
+
+    x_raw: optional [T, d] rows of another per-token tensor (the indexer's raw
+    keys) folded with the same block weights alpha and not rotated (the
+    indexer has no positional rotation); then (k_c, v_c, x_c) is returned.
     """
     k_raw = np.asarray(k_raw, dtype=np.float64)
     v_raw = np.asarray(v_raw, dtype=np.float64)
@@ -38,6 +42,9 @@ def compress(k_raw, v_raw, w_gate, m, pos0=0):
     nb = T // m
     k_c = np.zeros((nb, D))
     v_c = np.zeros((nb, D))
+    if x_raw is not None:
+        x_raw = np.asarray(x_raw, dtype=np.float64)
+        x_c = np.zeros((nb, x_raw.shape[1]))
     for i in range(nb):
         ks = k_raw[i * m:(i + 1) * m]
         vs = v_raw[i * m:(i + 1) * m]
@@ -47,6 +54,10 @@ def compress(k_raw, v_raw, w_gate, m, pos0=0):
         j = pos0 // m + i
         k_c[i] = apply_rope(alpha @ ks, j * m + m - 1)
         v_c[i] = alpha @ vs
+        if x_raw is not None:
+            x_c[i] = alpha @ x_raw[i * m:(i + 1) * m]
+    if x_raw is not None:
+        return k_c, v_c, x_c
     return k_c, v_c
 
 

@@ -10,6 +10,16 @@ e8m0      : OCP MX shared scale, 2**(E-127); E = 255 is NaN.
 MXFP4     : e2m1 elements, two per byte (element 2i in the low nibble), one
             e8m0 scale per 32 consecutive elements along the last dimension.
 
+Encoders (for compressed indexer keys written in these formats):
+  e4m3fn : round to nearest, ties to the even code (mantissa LSB 0), every
+           magnitude above 448 saturating to 448; the sign is kept (-0.0 for
+           negative values that round to zero).
+  MXFP4  : per 32 consecutive elements, amax = max |x|; the e8m0 code is
+           floor(log2 amax) - 2 + 127 clamped to 0..254 (0 when amax = 0), i.e.
+           the OCP MX rule that puts amax at 4..8 times the scale (e2m1's largest
+           exponent is 2); elements x / scale round to nearest e2m1, ties to the
+           even code, saturating at 6; the sign bit is x's (-0.0 -> code 8).
+
 Why these formats: [P1] section FP4 量化 says the indexer's QK path runs in FP4
 and that dequantising FP4 to FP8 loses nothing because fine-grained sub-block
 scales fit in FP8's range. A power-of-two (e8m0) scale makes that statement
@@ -94,3 +104,71 @@ def decode(arr, fmt, scales=None):
         assert scales is not None
         return mxfp4_to_f64(np.asarray(arr).view(np.uint8), np.asarray(scales).view(np.uint8))
     raise ValueError(fmt)
+
+
+# ------------------------------------------------------------------ encoders
+_E4M3_MAX = 448.0
+
+
+def f64_to_e4m3fn(x):
+    """float64 -> uint8 OCP e4m3fn codes (round to nearest even, saturating).
+
+    Works on the value's binary exponent: a normal result has 3 mantissa
+    bits below the leading one, so x is rounded to a multiple of 2**(e-3),
+    e = floor(log2 |x|); below 2**-6 the grid is the subnormal step 2**-9.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    assert not np.any(np.isnan(x)), "NaN has no saturating encoding here"
+    a = np.minimum(np.abs(x), _E4M3_MAX)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))       # a = f * 2**e2, f in [0.5, 1)
+    e = np.maximum(e2 - 1, -6)                       # exponent of the grid (subnormals share -6)
+    step = np.ldexp(1.0, (e - 3).astype(np.int64))
+    q = np.rint(a / step) * step                     # np.rint: ties to even multiple of step
+    q = np.minimum(q, _E4M3_MAX)
+    # encode the rounded magnitude q exactly
+    _, qe2 = np.frexp(np.where(q > 0, q, 1.0))
+    qe = qe2 - 1
+    normal = q >= 2.0 ** -6
+    mant_n = np.rint((q / np.ldexp(1.0, qe.astype(np.int64)) - 1.0) * 8).astype(np.int64)
+    code_n = ((qe + 7).astype(np.int64) << 3) | mant_n
+    code_s = np.rint(q / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    sign = np.where(np.signbit(x), 0x80, 0)
+    return (code | sign).astype(np.uint8)
+
+
+_E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def f64_to_e2m1(x):
+    """float64 (already divided by its scale) -> e2m1 codes 0..15, nearest,
+    ties to the even code, saturating at 6; bit 3 = sign bit of x."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    # distance to every magnitude; ties resolved toward the even code (the
+    # codes are in value order, so the candidates of a tie differ by one)
+    d = np.abs(a[..., None] - _E2M1_VALUES)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    codes = np.arange(8)
+    even_pick = np.where(cand & (codes % 2 == 0), codes, 99).min(axis=-1)
+    any_pick = np.where(cand, codes, 99).min(axis=-1)
+    c = np.where(even_pick < 99, even_pick, any_pick)
+    sign = np.where(np.signbit(x), 8, 0)
+    return (c | sign).astype(np.uint8)
+
+
+def f64_to_mxfp4(x):
+    """[..., n] float64 (n a multiple of 32) -> (packed [..., n/2] uint8,
+    scales [..., n/32] uint8 e8m0), element 2i in the low nibble."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % 32 == 0
+    blocks = x.reshape(x.shape[:-1] + (n // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e2 = np.frexp(np.where(amax > 0, amax, 1.0))
+    code = np.where(amax > 0, np.clip(e2 - 1 - 2 + 127, 0, 254), 0).astype(np.int64)
+    scale = np.ldexp(1.0, code - 127)
+    el = f64_to_e2m1(blocks / scale[..., None]).reshape(x.shape)
+    packed = (el[..., 0::2] | (el[..., 1::2] << 4)).astype(np.uint8)
+    return packed, code.astype(np.uint8)

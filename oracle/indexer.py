@@ -13,6 +13,10 @@ projections need trained weights, which are not part of this path).
 import numpy as np
 
 
+def _pos(q_pos0, b):
+    return int(q_pos0) if np.ndim(q_pos0) == 0 else int(np.asarray(q_pos0)[b])
+
+
 def index_scores(q_i, w_i, k_i):
     """Scores of one query against n entries.
 
@@ -30,7 +34,8 @@ def index_scores_batch(q_i, w_i, k_i, q_pos0, m):
 
     q_i [B, Lq, H_I, d_I], w_i [B, Lq, H_I], k_i [B, N, d_I] (float64).
     Returns [B, Lq, N]; query row i is at absolute position q_pos0 + i and
-    sees entries j < (q_pos0 + i + 1) // m.
+    sees entries j < (q_pos0 + i + 1) // m. q_pos0 is one position for the
+    batch or one per sequence ([B]).
     """
     q_i = np.asarray(q_i, dtype=np.float64)
     B, Lq = q_i.shape[:2]
@@ -38,7 +43,7 @@ def index_scores_batch(q_i, w_i, k_i, q_pos0, m):
     out = np.full((B, Lq, N), -np.inf)
     for b in range(B):
         for i in range(Lq):
-            n = (q_pos0 + i + 1) // m
+            n = (_pos(q_pos0, b) + i + 1) // m
             assert n <= N, "indexer key cache does not hold every visible entry"
             out[b, i, :n] = index_scores(q_i[b, i], w_i[b, i], k_i[b, :n])
     return out

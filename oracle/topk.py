@@ -28,12 +28,13 @@ def topk_select(scores, k):
 
 
 def topk_batch(scores, k, q_pos0, m):
-    """scores [B, Lq, N] -> idx [B, Lq, k]; query row i sees j < (q_pos0+i+1)//m."""
+    """scores [B, Lq, N] -> idx [B, Lq, k]; query row i sees j < (q_pos0+i+1)//m
+    (q_pos0 one position for the batch or one per sequence, [B])."""
     B, Lq, N = scores.shape
     out = np.full((B, Lq, k), -1, dtype=np.int64)
     for b in range(B):
         for i in range(Lq):
-            n = (q_pos0 + i + 1) // m
+            n = ((int(q_pos0) if np.ndim(q_pos0) == 0 else int(np.asarray(q_pos0)[b])) + i + 1) // m
             assert n <= N, "score row does not hold every visible entry"
             out[b, i] = topk_select(scores[b, i, :n], k)
     return out
