@@ -25,7 +25,7 @@
  *    two e2m1 codes per byte (element 2i in the low nibble) plus one e8m0
  *    scale byte (2^(E-127)) per 32 consecutive elements of the last dim.
  *  - Positions: one shared KV head; the query row i of every sequence sits at
- *    absolute position q_pos0 + i. Compressed entry j of a cache covers raw
+ *    absolute position q_pos0 + i (per sequence in the *_varlen calls). Compressed entry j of a cache covers raw
  *    positions j*m .. j*m+m-1 and is visible to a query at t iff j*m+m-1 <= t,
  *    i.e. for j < n(t) = (t+1)/m.
  *  - RoPE: on the last 64 dims of each head, interleaved pairs (2i, 2i+1),
@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum {
   CSA_F32 = 0,
@@ -245,6 +245,78 @@ int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dt
                    int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
                    const float* sink, void* out, float* lse,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Decode state cache and per-sequence positions.
+ * [P1] 框架層優化 (heterogeneous KV cache management): a state cache holding
+ * the sliding-window tokens and the tokens whose block is not yet compressed,
+ * kept apart from the classic cache of compressed entries; [P3] section 01,
+ * 异构缓存设计: the same heterogeneous KV cache layout for inference.
+ * [P1] 混合注意力機制: an entry exists once its block of m tokens is complete.
+ * Layout taken (the pages give none): per sequence a ring of R raw rows, the
+ * token at absolute position s in slot s % R, for K and V ([B, R, D], KV
+ * dtype) and optionally the indexer's raw key ([B, R, d_i], KV dtype).
+ *
+ * csa_state_append — one decode step: for each sequence b with t = pos[b] >= 0
+ * (a negative position marks an inactive slot: nothing is written), the rows
+ * k_new[b], v_new[b] (and ki_new[b]) go to slot t % R of the rings; when t+1
+ * is a multiple of m, the block t-m+1 .. t is folded from the ring into
+ * entry j = (t+1)/m - 1 exactly as csa_compress folds a block (gate
+ * <w_gate, K_raw[s]>, softmax weights alpha, K_c = RoPE(sum alpha K, t),
+ * V_c = sum alpha V), and, when d_i > 0, ki_c[b, j] = sum alpha KI (unrotated)
+ * stored in idx_dtype: f32; bf16 (nearest even); e4m3fn (nearest even,
+ * magnitudes above 448 saturate to 448); MXFP4 (per 32 elements the e8m0 code
+ * floor(log2 amax) - 2 + 127 clamped to 0..254, 0 for an all-zero block;
+ * elements nearest e2m1, ties to the even code, saturating at 6; sign bits
+ * copied). An entry with j >= N_cap is not written. The rows of
+ * t-m+1 .. t-1 must be in the ring (appended by earlier steps).
+ *
+ *   B, D, m, R     sequences, head dim (128 or 512), block (1..4096), ring
+ *                  slots (m <= R <= 2^24)
+ *   kv_dtype       CSA_F32 or CSA_BF16 (new rows, rings, k_c, v_c)
+ *   pos            [B] int64 device positions of the appended tokens
+ *   k_new, v_new   [B, D]; w_gate [D] float32
+ *   k_ring, v_ring [B, R, D]; k_c, v_c [B, N_cap, D]
+ *   d_i            0 (no indexer key) or 32, 64, 128
+ *   idx_dtype      storage of ki_c (any csa_dtype)
+ *   ki_new [B, d_i], ki_ring [B, R, d_i] (KV dtype); ki_c [B, N_cap, d_i]
+ *   (fp4: [B, N_cap, d_i/2] bytes) and ki_c_scale [B, N_cap, d_i/32] (fp4 only)
+ * A step reads the ring rows of earlier steps, so steps of one cache must be
+ * ordered on one stream. pos must be 8-byte aligned.
+ */
+int csa_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* pos,
+                     const void* k_new, const void* v_new, const float* w_gate,
+                     void* k_ring, void* v_ring, void* k_c, void* v_c, int64_t N_cap,
+                     int d_i, int idx_dtype, const void* ki_new, void* ki_ring, void* ki_c,
+                     uint8_t* ki_c_scale, void* stream);
+
+/*
+ * csa_index_topk_varlen, csa_sparse_attn_varlen, hca_dense_attn_varlen — the
+ * calls above with a position per sequence: query row i of sequence b is at
+ * t = min(max(q_pos[b], 0), q_pos_max) + i (q_pos [B] int64 device memory;
+ * q_pos_max, a host bound of the positions, sizes the grids and takes the
+ * place of q_pos0 in the limits and the *_ws_bytes queries). The attention
+ * calls read the window rows from the state cache's rings (R slots, position
+ * s in slot s % R; requires W + Lq - 1 <= R, and the ring must hold positions
+ * max(0, t-W+1) .. t of every query). Everything else is as in the uniform
+ * call.
+ */
+int csa_index_topk_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int m, int64_t N_cap,
+                          int H_i, int d_i, int idx_dtype,
+                          const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                          const void* k_i, const uint8_t* k_i_scale,
+                          int topk, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+int csa_sparse_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int H, int D, int kv_dtype,
+                           const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                           int topk, const int32_t* idx,
+                           int R, const void* k_ring, const void* v_ring, int W,
+                           const float* sink, void* out, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+int hca_dense_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int m, int H, int D,
+                          int kv_dtype, const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                          int R, const void* k_ring, const void* v_ring, int W,
+                          const float* sink, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,14 @@ SIGNATURES = {
     "hca_dense_attn_ws_bytes": (_Z, [_I, _I, _L, _I, _I, _I, _I]),
     "hca_dense_attn": (_I, [_I, _I, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _L, _P, _P, _I,
                             _P, _P, _P, _P, _Z, _P]),
+    "csa_state_append": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _L, _I, _I,
+                              _P, _P, _P, _P, _P]),
+    "csa_index_topk_varlen": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P,
+                                   _Z, _P]),
+    "csa_sparse_attn_varlen": (_I, [_I, _I, _P, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _P, _P, _I,
+                                    _P, _P, _P, _P, _Z, _P]),
+    "hca_dense_attn_varlen": (_I, [_I, _I, _P, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _P, _P, _I,
+                                   _P, _P, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -229,4 +237,74 @@ def hca_attn(q, k_c, v_c, m, k_raw, v_raw, raw_pos0, W, sink, q_pos0, ws=None, o
                                 _ptr(v_c), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W,
                                 _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream()))
+    return out, lse
+
+
+# ------------------------------------------------- decode state cache, varlen
+def _pos_tensor(pos):
+    if pos.dtype != torch.int64:
+        raise CSAError("positions must be int64")
+    return _ptr(pos)
+
+
+def state_append(pos, k_new, v_new, w_gate, m, k_ring, v_ring, k_c, v_c,
+                 ki_new=None, ki_ring=None, ki_c=None, ki_scale=None, idx_fmt="bf16"):
+    """One decode step of the state cache: token rows k_new, v_new [B, D]
+    (and ki_new [B, d_i]) at positions pos [B] int64 enter the rings
+    k_ring, v_ring [B, R, D] (ki_ring [B, R, d_i]); blocks they complete are
+    compressed into k_c, v_c [B, N_cap, D] (ki_c in idx_fmt, + ki_scale for
+    fp4). Negative positions are skipped."""
+    B, D = k_new.shape
+    R = k_ring.shape[1]
+    d_i = 0 if ki_new is None else ki_new.shape[1]
+    _check(lib().csa_state_append(B, D, m, R, _kv_dtype(k_new), _pos_tensor(pos), _ptr(k_new), _ptr(v_new),
+                                  _ptr(w_gate), _ptr(k_ring), _ptr(v_ring), _ptr(k_c), _ptr(v_c), k_c.shape[1],
+                                  d_i, IDX_FORMATS[idx_fmt], _ptr(ki_new), _ptr(ki_ring), _ptr(ki_c),
+                                  _ptr(ki_scale), _stream()))
+
+
+def index_topk_varlen(q_i, w_i, k_i, topk, q_pos, q_pos_max, m, fmt, q_scale=None, k_scale=None,
+                      ws=None, out=None):
+    """index_topk with query row 0 of sequence b at q_pos[b] (int64 [B] on
+    the GPU, bounded by the host value q_pos_max)."""
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if ws is None:
+        ws = _ws(index_topk_ws_bytes(B, Lq, q_pos_max, m, N_cap, topk), q_i.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk), dtype=torch.int32, device=q_i.device)
+    _check(lib().csa_index_topk_varlen(B, Lq, _pos_tensor(q_pos), q_pos_max, m, N_cap, H_i, d_i,
+                                       IDX_FORMATS[fmt], _ptr(q_i), _ptr(q_scale), _ptr(w_i), _ptr(k_i),
+                                       _ptr(k_scale), topk, _ptr(out), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def sparse_attn_varlen(q, k_c, v_c, idx, k_ring, v_ring, W, sink, q_pos, q_pos_max, ws=None, out=None,
+                       lse=None):
+    """sparse_attn with per-sequence positions q_pos [B] int64 (bound
+    q_pos_max) and the window read from the state cache's rings [B, R, D]."""
+    B, Lq, H, D = q.shape
+    topk_ = idx.shape[-1]
+    if ws is None:
+        ws = _ws(sparse_attn_ws_bytes(B, Lq, H, D, topk_, W), q.device)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().csa_sparse_attn_varlen(B, Lq, _pos_tensor(q_pos), q_pos_max, H, D, _kv_dtype(q), _ptr(q),
+                                        k_c.shape[1], _ptr(k_c), _ptr(v_c), topk_, _ptr(idx), k_ring.shape[1],
+                                        _ptr(k_ring), _ptr(v_ring), W, _ptr(sink), _ptr(out), _ptr(lse),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+    return out, lse
+
+
+def hca_attn_varlen(q, k_c, v_c, m, k_ring, v_ring, W, sink, q_pos, q_pos_max, ws=None, out=None, lse=None):
+    """hca_attn with per-sequence positions and the window from the rings."""
+    B, Lq, H, D = q.shape
+    if ws is None:
+        ws = _ws(hca_attn_ws_bytes(B, Lq, q_pos_max, m, H, D, W), q.device)
+    out, lse = _alloc_out(q, out, lse)
+    _check(lib().hca_dense_attn_varlen(B, Lq, _pos_tensor(q_pos), q_pos_max, m, H, D, _kv_dtype(q), _ptr(q),
+                                       k_c.shape[1], _ptr(k_c), _ptr(v_c), k_ring.shape[1], _ptr(k_ring),
+                                       _ptr(v_ring), W, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream()))
     return out, lse

@@ -16,9 +16,11 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 // Visible compressed entries of the last query row.
 inline int64_t n_last(int64_t q_pos0, int Lq, int m) { return (q_pos0 + Lq) / m; }
 
-int check_window(int Lq, int64_t q_pos0, int W, int T_raw, int64_t raw_pos0) {
+int check_window(int Lq, int64_t q_pos0, int W, int T_raw, int64_t raw_pos0, bool ring) {
   if (W < 0 || W > 1024 || T_raw < 0) return CSA_ERR_SHAPE;
   if (W == 0) return CSA_OK;
+  // a ring holds every query's window: W + Lq - 1 distinct positions
+  if (ring) return (int64_t)W + Lq - 1 <= T_raw ? CSA_OK : CSA_ERR_SHAPE;
   const int64_t lo = q_pos0 - W + 1 > 0 ? q_pos0 - W + 1 : 0;
   if (raw_pos0 < 0 || raw_pos0 > lo) return CSA_ERR_SHAPE;
   if (q_pos0 + Lq - 1 >= raw_pos0 + T_raw) return CSA_ERR_SHAPE;
@@ -79,6 +81,26 @@ static size_t scores_bytes(int B, int Lq, int64_t N_cap) {
   return ((size_t)B * Lq * N_cap * sizeof(float) + 255) / 256 * 256;
 }
 
+int csa_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* pos, const void* k_new,
+                     const void* v_new, const float* w_gate, void* k_ring, void* v_ring, void* k_c, void* v_c,
+                     int64_t N_cap, int d_i, int idx_dtype, const void* ki_new, void* ki_ring, void* ki_c,
+                     uint8_t* ki_c_scale, void* stream) {
+  if (!pos || !k_new || !v_new || !w_gate || !k_ring || !v_ring || !k_c || !v_c) return CSA_ERR_NULL;
+  if (d_i > 0 && (!ki_new || !ki_ring || !ki_c)) return CSA_ERR_NULL;
+  if (d_i > 0 && idx_dtype == CSA_FP4_E2M1 && !ki_c_scale) return CSA_ERR_NULL;
+  if (!kv_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (d_i > 0 && (idx_dtype < CSA_F32 || idx_dtype > CSA_FP4_E2M1)) return CSA_ERR_DTYPE;
+  if (B < 0 || !head_dim_ok(D) || m < 1 || m > 4096 || R < m || R > (1 << 24) || N_cap < 1) return CSA_ERR_SHAPE;
+  if (!(d_i == 0 || d_i == 32 || d_i == 64 || d_i == 128)) return CSA_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(w_gate) || !aligned16(k_ring) || !aligned16(v_ring) ||
+      !aligned16(k_c) || !aligned16(v_c) || ((uintptr_t)pos & 7u) ||
+      (d_i > 0 && (!aligned16(ki_new) || !aligned16(ki_ring) || !aligned16(ki_c))))
+    return CSA_ERR_ALIGN;
+  return launch_state_append(B, D, m, R, kv_dtype, pos, k_new, v_new, w_gate, k_ring, v_ring, k_c, v_c, N_cap,
+                             d_i, idx_dtype, ki_new, ki_ring, ki_c, ki_c_scale, as_stream(stream))
+             ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
 // Fused indexer + per-chunk top-k: candidate lists of the chunks of kIdxColsPerWG
 // entries, merged by the top-k merge levels.
 static size_t fused_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
@@ -91,14 +113,14 @@ static bool use_fused(int Lq, int H_i, int topk) {
   return (index_qk_queries_per_group(H_i) == 1 || Lq == 1) && 4 * topk <= index_qk_list_len();
 }
 
-static int launch_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
-                             int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+static int launch_candidates(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
+                             int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
                              const void* k_i, const uint8_t* k_i_scale, int topk, void* cand, hipStream_t st) {
   const int64_t rows = (int64_t)B * Lq;
   uint32_t* ck = (uint32_t*)cand;
   int32_t* ci = (int32_t*)(ck + rows * index_qk_nchunks(q_pos0, Lq, m) * topk);
-  return launch_index_qk_fused(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
-                               topk, ck, ci, st);
+  return launch_index_qk_fused(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                               k_i_scale, topk, ck, ci, st);
 }
 
 size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
@@ -137,14 +159,16 @@ int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_
                              k_i_scale, 1))
     return rc;
   if (!aligned16(scores)) return CSA_ERR_ALIGN;
-  return launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+  return launch_index_qk(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                          k_i_scale, scores, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
-int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
-                   int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
-                   const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
-                   size_t ws_bytes, void* stream) {
+// csa_index_topk and csa_index_topk_varlen: q_pos == nullptr means every
+// sequence's row 0 is at q_pos0; otherwise q_pos0 bounds the q_pos values.
+static int index_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
+                      int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                      const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
+                      size_t ws_bytes, void* stream) {
   if (!idx_out) return CSA_ERR_NULL;
   if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                              k_i_scale, topk))
@@ -154,18 +178,35 @@ int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i,
   if ((int64_t)B * Lq == 0) return CSA_OK;
   hipStream_t st = as_stream(stream);
   if (use_fused(Lq, H_i, topk)) {
-    if (launch_candidates(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
-                          topk, ws, st))
+    if (launch_candidates(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                          k_i_scale, topk, ws, st))
       return CSA_ERR_LAUNCH;
     return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, ws, idx_out, st)
                ? CSA_ERR_LAUNCH : CSA_OK;
   }
   float* scores = (float*)ws;
   void* cand = (char*)ws + scores_bytes(B, Lq, N_cap);
-  if (launch_index_qk(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+  if (launch_index_qk(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                       k_i_scale, scores, st))
     return CSA_ERR_LAUNCH;
-  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, cand, st) ? CSA_ERR_LAUNCH : CSA_OK;
+  return launch_topk(B, Lq, q_pos0, q_pos, m, N_cap, scores, topk, idx_out, cand, st) ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                   int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                   const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return index_topk(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
+                    topk, idx_out, ws, ws_bytes, stream);
+}
+
+int csa_index_topk_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int m, int64_t N_cap,
+                          int H_i, int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale,
+                          const float* w_i, const void* k_i, const uint8_t* k_i_scale, int topk,
+                          int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_pos) return CSA_ERR_NULL;
+  return index_topk(B, Lq, q_pos_max, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
+                    topk, idx_out, ws, ws_bytes, stream);
 }
 
 int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
@@ -174,7 +215,7 @@ int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* s
   if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
   if (!aligned16(scores) || !aligned16(idx_out) || !aligned16(ws)) return CSA_ERR_ALIGN;
   if (!ws || ws_bytes < csa_topk_ws_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
-  return launch_topk(B, Lq, q_pos0, m, N_cap, scores, topk, idx_out, ws, as_stream(stream))
+  return launch_topk(B, Lq, q_pos0, nullptr, m, N_cap, scores, topk, idx_out, ws, as_stream(stream))
              ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
@@ -195,8 +236,8 @@ int csa_index_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, in
   if (!aligned16(cand)) return CSA_ERR_ALIGN;
   if (cand_bytes < csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
-  return launch_candidates(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale, topk,
-                           cand, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+  return launch_candidates(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                           k_i_scale, topk, cand, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, size_t cand_bytes,
@@ -214,12 +255,12 @@ int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, s
 static int check_attn_common(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
                              const void* k_c, const void* v_c, int T_raw, int64_t raw_pos0,
                              const void* k_raw, const void* v_raw, int W, const float* sink,
-                             void* out, float* lse, void* ws, int64_t N_cap) {
+                             void* out, float* lse, void* ws, int64_t N_cap, bool ring) {
   if (!q || !k_c || !v_c || !out) return CSA_ERR_NULL;
   if (W > 0 && (!k_raw || !v_raw)) return CSA_ERR_NULL;
   if (!kv_ok(kv_dtype)) return CSA_ERR_DTYPE;
   if (B < 0 || Lq < 0 || q_pos0 < 0 || H < 1 || H > 128 || !head_dim_ok(D) || N_cap < 1) return CSA_ERR_SHAPE;
-  if (int rc = check_window(Lq, q_pos0, W, T_raw, raw_pos0)) return rc;
+  if (int rc = check_window(Lq, q_pos0, W, T_raw, raw_pos0, ring)) return rc;
   if (!aligned16(q) || !aligned16(k_c) || !aligned16(v_c) || !aligned16(out) || !aligned16(ws) ||
       (W > 0 && (!aligned16(k_raw) || !aligned16(v_raw))))
     return CSA_ERR_ALIGN;
@@ -238,21 +279,24 @@ size_t csa_sparse_attn_ws_bytes(int B, int Lq, int H, int D, int topk, int W) {
   return split > dec ? split : dec;
 }
 
-int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
-                    int64_t N_cap, const void* k_c, const void* v_c, int topk, const int32_t* idx,
-                    int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
-                    const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
-                    void* stream) {
+// csa_sparse_attn and csa_sparse_attn_varlen (q_pos != nullptr: per-sequence
+// positions bounded by q_pos0, raw rows in a ring of T_raw slots).
+static int sparse_attn(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int H, int D, int kv_dtype,
+                       const void* q, int64_t N_cap, const void* k_c, const void* v_c, int topk,
+                       const int32_t* idx, int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw,
+                       int W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
+  const bool ring = q_pos != nullptr;
   if (topk > 0 && !idx) return CSA_ERR_NULL;
   if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw,
-                                 v_raw, W, sink, out, lse, ws, N_cap))
+                                 v_raw, W, sink, out, lse, ws, N_cap, ring))
     return rc;
   if (topk < 0 || topk > 2048) return CSA_ERR_SHAPE;
   if (!ws || ws_bytes < csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W)) return CSA_ERR_WORKSPACE;
   AttnArgs a{};
-  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
-  a.k_c = k_c; a.v_c = v_c; a.topk = topk; a.idx = idx; a.T_raw = T_raw; a.raw_pos0 = raw_pos0;
-  a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
+  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.q_pos = q_pos; a.m = 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
+  a.k_c = k_c; a.v_c = v_c; a.topk = topk; a.idx = idx; a.T_raw = T_raw; a.raw_pos0 = ring ? 0 : raw_pos0;
+  a.ring = ring; a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
   if (attn_decode_eligible(kv_dtype, false, H, D) && topk + W > 0)
     return launch_attn_decode(a, ws, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
   a.nsplit_max = attn_nsplit_max_csa(topk, W);
@@ -262,30 +306,68 @@ int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, c
   return launch_attn(a, kv_dtype, false, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
+int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
+                    int64_t N_cap, const void* k_c, const void* v_c, int topk, const int32_t* idx,
+                    int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                    const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  return sparse_attn(B, Lq, q_pos0, nullptr, H, D, kv_dtype, q, N_cap, k_c, v_c, topk, idx, T_raw, raw_pos0,
+                     k_raw, v_raw, W, sink, out, lse, ws, ws_bytes, stream);
+}
+
+int csa_sparse_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int H, int D, int kv_dtype,
+                           const void* q, int64_t N_cap, const void* k_c, const void* v_c, int topk,
+                           const int32_t* idx, int R, const void* k_ring, const void* v_ring, int W,
+                           const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
+  if (!q_pos) return CSA_ERR_NULL;
+  return sparse_attn(B, Lq, q_pos_max, q_pos, H, D, kv_dtype, q, N_cap, k_c, v_c, topk, idx, R, 0, k_ring,
+                     v_ring, W, sink, out, lse, ws, ws_bytes, stream);
+}
+
 size_t hca_dense_attn_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int W) {
   if (B <= 0 || Lq <= 0 || m < 1 || W < 0 || q_pos0 < 0) return 16;
   return attn_ws(B, Lq, H, D, attn_nsplit_max_hca(q_pos0, Lq, m, W), 4);
+}
+
+// hca_dense_attn and hca_dense_attn_varlen (as sparse_attn above).
+static int dense_attn(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int H, int D, int kv_dtype,
+                      const void* q, int64_t N_cap, const void* k_c, const void* v_c, int T_raw,
+                      int64_t raw_pos0, const void* k_raw, const void* v_raw, int W, const float* sink,
+                      void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const bool ring = q_pos != nullptr;
+  if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw,
+                                 v_raw, W, sink, out, lse, ws, N_cap, ring))
+    return rc;
+  if (m < 1 || m > 4096) return CSA_ERR_SHAPE;
+  if (n_last(q_pos0, Lq, m) > N_cap || n_last(q_pos0, Lq, m) + W > (int64_t)1 << 30) return CSA_ERR_SHAPE;
+  if (!ws || ws_bytes < hca_dense_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W)) return CSA_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.q_pos = q_pos; a.m = m; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
+  a.k_c = k_c; a.v_c = v_c; a.topk = 0; a.idx = nullptr; a.T_raw = T_raw; a.raw_pos0 = ring ? 0 : raw_pos0;
+  a.ring = ring; a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
+  a.nsplit_max = attn_nsplit_max_hca(q_pos0, Lq, m, W);
+  const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
+  a.ws_o = ws;
+  a.ws_ml = (float*)((char*)ws + (slots * D * (kv_dtype == CSA_F32 ? 4 : 2) + 15) / 16 * 16);
+  return launch_attn(a, kv_dtype, true, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 int hca_dense_attn(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype, const void* q,
                    int64_t N_cap, const void* k_c, const void* v_c, int T_raw, int64_t raw_pos0,
                    const void* k_raw, const void* v_raw, int W, const float* sink, void* out,
                    float* lse, void* ws, size_t ws_bytes, void* stream) {
-  if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw,
-                                 v_raw, W, sink, out, lse, ws, N_cap))
-    return rc;
-  if (m < 1 || m > 4096) return CSA_ERR_SHAPE;
-  if (n_last(q_pos0, Lq, m) > N_cap || n_last(q_pos0, Lq, m) + W > (int64_t)1 << 30) return CSA_ERR_SHAPE;
-  if (!ws || ws_bytes < hca_dense_attn_ws_bytes(B, Lq, q_pos0, m, H, D, W)) return CSA_ERR_WORKSPACE;
-  AttnArgs a{};
-  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = m; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
-  a.k_c = k_c; a.v_c = v_c; a.topk = 0; a.idx = nullptr; a.T_raw = T_raw; a.raw_pos0 = raw_pos0;
-  a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
-  a.nsplit_max = attn_nsplit_max_hca(q_pos0, Lq, m, W);
-  const size_t slots = (size_t)B * Lq * a.nsplit_max * H;
-  a.ws_o = ws;
-  a.ws_ml = (float*)((char*)ws + (slots * D * (kv_dtype == CSA_F32 ? 4 : 2) + 15) / 16 * 16);
-  return launch_attn(a, kv_dtype, true, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+  return dense_attn(B, Lq, q_pos0, nullptr, m, H, D, kv_dtype, q, N_cap, k_c, v_c, T_raw, raw_pos0, k_raw, v_raw,
+                    W, sink, out, lse, ws, ws_bytes, stream);
+}
+
+int hca_dense_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int m, int H, int D,
+                          int kv_dtype, const void* q, int64_t N_cap, const void* k_c, const void* v_c, int R,
+                          const void* k_ring, const void* v_ring, int W, const float* sink, void* out,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_pos) return CSA_ERR_NULL;
+  return dense_attn(B, Lq, q_pos_max, q_pos, m, H, D, kv_dtype, q, N_cap, k_c, v_c, R, 0, k_ring, v_ring, W, sink,
+                    out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

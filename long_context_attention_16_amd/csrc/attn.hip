@@ -101,7 +101,7 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 }
 
 struct SplitInfo {
-  int64_t t, lo;
+  int64_t t, lo, row_lo;  // row_lo: raw row of window position lo
   int b, n_c, n_w, s0, s1;
 };
 
@@ -125,7 +125,7 @@ __device__ __forceinline__ int row_source(const AttnArgs& p, const SplitInfo& si
   const bool wok = sp - si.n_c < si.n_w;
   const int kind = !in_split ? 0 : (comp ? (jok ? 1 : 0) : (wok ? 2 : 0));
   *src = kind == 1 ? ((int64_t)si.b * p.N_cap + j) * D
-                   : (kind == 2 ? ((int64_t)si.b * p.T_raw + (wpos - p.raw_pos0)) * D : 0);
+                   : (kind == 2 ? ((int64_t)si.b * p.T_raw + attn_window_row(p, si.row_lo, sp - si.n_c)) * D : 0);
   *pos = kind == 2 ? wpos : 0;
   return kind;
 }
@@ -450,9 +450,10 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   SplitInfo si;
   si.b = qrow / p.Lq;
   const int i = qrow % p.Lq;
-  si.t = p.q_pos0 + i;
+  si.t = seq_pos(p.q_pos, p.q_pos0, si.b) + i;
   si.n_c = HCA ? (int)((si.t + 1) / p.m) : p.topk;
   si.lo = si.t - p.W + 1 > 0 ? si.t - p.W + 1 : 0;
+  si.row_lo = attn_raw_row(p, si.lo);
   si.n_w = p.W > 0 ? (int)(si.t - si.lo + 1) : 0;
   const int S = si.n_c + p.W;
   const int CH = attn_split_rows(S);
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs p) 
   const int64_t qrow = row / p.H;
   const int h = (int)(row % p.H);
   const int i = (int)(qrow % p.Lq);
-  const int64_t t = p.q_pos0 + i;
+  const int64_t t = seq_pos(p.q_pos, p.q_pos0, (int)(qrow / p.Lq)) + i;
   const int n_c = HCA ? (int)((t + 1) / p.m) : p.topk;
   const int nsplit = attn_nsplit(n_c + p.W);
   if (nsplit == 1) return;

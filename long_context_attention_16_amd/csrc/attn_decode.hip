@@ -67,30 +67,31 @@ __device__ __forceinline__ const int32_t* idx_slot(const AttnArgs& p, int qrow, 
 }
 
 // Source of slot sp given its idx value j (idx_slot).
-__device__ __forceinline__ int dec_source(const AttnArgs& p, int b, int64_t lo, int n_w, int sp, int32_t jv,
-                                          int64_t* src, int64_t* pos) {
+__device__ __forceinline__ int dec_source(const AttnArgs& p, int b, int64_t lo, int64_t row_lo, int n_w, int sp,
+                                          int32_t jv, int64_t* src, int64_t* pos) {
   const int64_t j = p.topk > 0 ? (int64_t)jv : -1;
   const int w = sp - p.topk;
   const bool comp = sp < p.topk && j >= 0 && j < p.N_cap;
   const bool win = sp >= p.topk && w < n_w;
   *pos = win ? lo + w : 0;
   *src = comp ? ((int64_t)b * p.N_cap + j) * kDecD
-       : win ? ((int64_t)b * p.T_raw + (lo + w - p.raw_pos0)) * kDecD
+       : win ? ((int64_t)b * p.T_raw + attn_window_row(p, row_lo, w)) * kDecD
              : (int64_t)b * p.N_cap * kDecD;
   return comp ? 1 : win ? 2 : 0;
 }
 
 struct DecQuery {
   int b, n_w;
-  int64_t t, lo;
+  int64_t t, lo, row_lo;  // row_lo: raw row of window position lo
 };
 
 __device__ __forceinline__ DecQuery dec_query(const AttnArgs& p, int qrow) {
   DecQuery d;
   d.b = qrow / p.Lq;
-  d.t = p.q_pos0 + qrow % p.Lq;
+  d.t = seq_pos(p.q_pos, p.q_pos0, d.b) + qrow % p.Lq;
   d.lo = d.t - p.W + 1 > 0 ? d.t - p.W + 1 : 0;
   d.n_w = p.W > 0 ? (int)(d.t - d.lo + 1) : 0;
+  d.row_lo = attn_raw_row(p, d.lo);
   return d;
 }
 
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int
 #pragma unroll
   for (int s = 0; s < QS; ++s) qraw[s] = *reinterpret_cast<const uint4*>(qb + 32 * s + 8 * g);
   int64_t src, pos;
-  const int kd = dec_source(p, dq.b, dq.lo, dq.n_w, su, jv, &src, &pos);
+  const int kd = dec_source(p, dq.b, dq.lo, dq.row_lo, dq.n_w, su, jv, &src, &pos);
   if (tid < kRopePairs) rope_cos_sin_f(dq.t, rev, &qcos[tid], &qsin[tid]);
   if (tid < kArows) {
     kind[tid] = kd;

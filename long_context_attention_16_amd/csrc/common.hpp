@@ -95,6 +95,16 @@ __device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* 
 // every negative value (and -0) a negative int32, so they become +0 and
 // everything else passes unchanged. fmaxf on a value the compiler cannot
 // prove quiet costs an extra canonicalizing max in IEEE mode.
+// Absolute position of query row 0 of sequence b: `bound` for every
+// sequence, or q_pos[b] clamped into [0, bound] when per-sequence positions
+// are given (q_pos != nullptr; bound is then their upper bound, which sized
+// the grid and the workspace).
+__device__ __forceinline__ int64_t seq_pos(const int64_t* q_pos, int64_t bound, int b) {
+  if (q_pos == nullptr) return bound;
+  const int64_t v = q_pos[b];
+  return v < 0 ? 0 : (v > bound ? bound : v);
+}
+
 __device__ __forceinline__ float relu_bits(float x) {
   const int v = __builtin_bit_cast(int, x);
   return __builtin_bit_cast(float, v > 0 ? v : 0);

@@ -47,6 +47,26 @@ template <> struct RowIO<uint16_t, 8> {
   }
 };
 
+template <> struct RowIO<float, 2> {
+  static __device__ __forceinline__ void load(const float* p, float* v) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  }
+  static __device__ __forceinline__ void store(float* p, const float* v) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+};
+template <> struct RowIO<uint16_t, 2> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float* v) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_bits_to_f32((uint16_t)(w & 0xFFFF));
+    v[1] = bf16_bits_to_f32((uint16_t)(w >> 16));
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, const float* v) {
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+  }
+};
+
 constexpr int kCompressWaves = 4;
 
 template <typename T, int VEC>
@@ -222,6 +242,210 @@ __global__ __launch_bounds__(kCompressWaves * kWave) void compress_d128_kernel(
   const int64_t orow = (int64_t)b * N_cap + j;
   RowIO<T, VEC>::store(k_c + orow * D + c0, ak);
   RowIO<T, VEC>::store(v_c + orow * D + c0, av);
+}
+
+// ------------------------------------------------------------ state append
+//
+// One decode step of the state cache: the token at position t = pos[b] of
+// each sequence enters slot t % R of the sequence's ring of raw rows (K, V
+// and the indexer's raw key); when it completes a block (t + 1 a multiple of
+// m) the block's m rows are folded into entry j = (t + 1) / m - 1 exactly as
+// compress_kernel folds a block (same online softmax, RoPE at position t),
+// and the indexer key is folded with the same weights, unrotated, and stored
+// in the indexer's format. Source: "DeepSeek V4 重磅開源！…" (InfoQ), section
+// 框架層優化 (a state cache of window tokens and not-yet-compressed tokens,
+// kept apart from the compressed KV cache), and section 混合注意力機制 (an
+// entry exists once its block is complete).
+//
+// One wave per sequence: lane l owns channels VEC*l .. VEC*l + VEC - 1 of
+// the K and V rows (VEC = D / 64) and channels 2l, 2l + 1 of the indexer key
+// (lanes l < d_i / 2). The token's own row is folded from registers, not
+// read back from the ring.
+
+// e4m3fn code of x: round to nearest even on the grid of x's binary exponent
+// (3 mantissa bits; the subnormal step 2^-9 below 2^-6), every magnitude
+// above 448 saturating to 448; the sign bit is x's.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  int e;
+  frexpf(a, &e);                                  // a = f * 2^e, f in [0.5, 1)
+  const int ge = a < 0.015625f ? -6 : e - 1;      // grid exponent
+  const float q = rintf(ldexpf(a, 3 - ge));       // multiples of 2^(ge - 3), 0 .. 16
+  // q in [8, 16] for a normal grid (16 carries into the next exponent),
+  // [0, 8] on the subnormal grid; both map to 8 * ge + 48 + q
+  return sign | (uint32_t)(8 * ge + 48 + (int)q);
+}
+
+// e2m1 code of x (already divided by its scale): nearest of 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6, ties to the even code, saturating at 6; the sign bit is x's.
+// The thresholds are the midpoints, each strict or not by the tie rule.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
+  return c | ((__builtin_bit_cast(uint32_t, x) >> 28) & 0x8u);
+}
+
+struct StateArgs {
+  int B, m, R, d_i, idx_fmt;
+  int64_t N_cap;
+  const int64_t* pos;
+  const void *k_new, *v_new, *ki_new;
+  const float* w_gate;
+  void *k_ring, *v_ring, *ki_ring, *k_c, *v_c, *ki_c;
+  uint8_t* ki_sc;
+};
+
+constexpr int kAppendWaves = 4;
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kAppendWaves * kWave) void state_append_kernel(StateArgs a) {
+  constexpr int D = VEC * kWave;
+  const int lane = threadIdx.x % kWave;
+  const int b = blockIdx.x * kAppendWaves + threadIdx.x / kWave;
+  if (b >= a.B) return;
+  const int64_t t = a.pos[b];
+  if (t < 0) return;  // an inactive slot of the batch
+  const int c0 = lane * VEC;
+  const bool xl = lane < a.d_i / 2;  // lane holds indexer-key channels
+  const T* kn_p = (const T*)a.k_new + (int64_t)b * D + c0;
+  const T* vn_p = (const T*)a.v_new + (int64_t)b * D + c0;
+  const int64_t slot_t = t % a.R;
+  T* kr = (T*)a.k_ring + (int64_t)b * a.R * D + c0;
+  T* vr = (T*)a.v_ring + (int64_t)b * a.R * D + c0;
+  T* xr = (T*)a.ki_ring + (int64_t)b * a.R * a.d_i + 2 * lane;
+  float kn[VEC], vn[VEC], xn[2] = {0.f, 0.f};
+  RowIO<T, VEC>::load(kn_p, kn);
+  RowIO<T, VEC>::load(vn_p, vn);
+  if (xl) RowIO<T, 2>::load((const T*)a.ki_new + (int64_t)b * a.d_i + 2 * lane, xn);
+  RowIO<T, VEC>::store(kr + slot_t * D, kn);
+  RowIO<T, VEC>::store(vr + slot_t * D, vn);
+  if (xl) RowIO<T, 2>::store(xr + slot_t * a.d_i, xn);
+
+  const int m = a.m;
+  if ((t + 1) % m != 0) return;  // no block completed
+  const int64_t j = (t + 1) / m - 1;
+  if (j >= a.N_cap) return;
+
+  float wg[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) wg[e] = a.w_gate[c0 + e];
+  float ak[VEC], av[VEC], ax[2] = {0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { ak[e] = 0.f; av[e] = 0.f; }
+  float run_max = -INFINITY, run_sum = 0.f;
+  auto fold = [&](const float (&kv)[VEC], const float (&vv)[VEC], const float (&xv)[2]) {
+    float g = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) g = fmaf(wg[e], kv[e], g);
+    g = wave_sum(g);
+    const float nmax = fmaxf(run_max, g);
+    const float scale = __expf(run_max - nmax);  // 0 on the first row
+    const float p = __expf(g - nmax);
+    run_sum = fmaf(run_sum, scale, p);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      ak[e] = fmaf(ak[e], scale, p * kv[e]);
+      av[e] = fmaf(av[e], scale, p * vv[e]);
+    }
+    ax[0] = fmaf(ax[0], scale, p * xv[0]);
+    ax[1] = fmaf(ax[1], scale, p * xv[1]);
+    run_max = nmax;
+  };
+  // rows t - m + 1 .. t - 1 from the ring (slots wrap once at most per row
+  // step), four loaded before the first of them is folded; then the new row
+  int64_t slot = (t - m + 1) % a.R;
+  auto next = [&](int64_t sl) { return sl + 1 == a.R ? (int64_t)0 : sl + 1; };
+  constexpr int kAhead = 4;
+  int s = 0;
+  for (; s + kAhead <= m - 1; s += kAhead) {
+    float kv[kAhead][VEC], vv[kAhead][VEC], xv[kAhead][2];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      RowIO<T, VEC>::load(kr + slot * D, kv[u]);
+      RowIO<T, VEC>::load(vr + slot * D, vv[u]);
+      xv[u][0] = 0.f; xv[u][1] = 0.f;
+      if (xl) RowIO<T, 2>::load(xr + slot * a.d_i, xv[u]);
+      slot = next(slot);
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) fold(kv[u], vv[u], xv[u]);
+  }
+  for (; s < m - 1; ++s) {
+    float kv[VEC], vv[VEC], xv[2] = {0.f, 0.f};
+    RowIO<T, VEC>::load(kr + slot * D, kv);
+    RowIO<T, VEC>::load(vr + slot * D, vv);
+    if (xl) RowIO<T, 2>::load(xr + slot * a.d_i, xv);
+    slot = next(slot);
+    fold(kv, vv, xv);
+  }
+  fold(kn, vn, xn);
+  const float inv = 1.0f / run_sum;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { ak[e] *= inv; av[e] *= inv; }
+  ax[0] *= inv;
+  ax[1] *= inv;
+  if (c0 >= D - kRopeDims) {  // RoPE on the folded key at the block's last position t
+#pragma unroll
+    for (int e = 0; e < VEC; e += 2) {
+      const int pair = (c0 + e - (D - kRopeDims)) / 2;
+      float cs, sn;
+      rope_cos_sin(t, pair, &cs, &sn);
+      const float x0 = ak[e], x1 = ak[e + 1];
+      ak[e] = x0 * cs - x1 * sn;
+      ak[e + 1] = x0 * sn + x1 * cs;
+    }
+  }
+  const int64_t orow = (int64_t)b * a.N_cap + j;
+  RowIO<T, VEC>::store((T*)a.k_c + orow * D + c0, ak);
+  RowIO<T, VEC>::store((T*)a.v_c + orow * D + c0, av);
+  if (a.d_i == 0) return;
+  // the indexer key in its storage format
+  if (a.idx_fmt == 0) {
+    if (xl) RowIO<float, 2>::store((float*)a.ki_c + orow * a.d_i + 2 * lane, ax);
+  } else if (a.idx_fmt == 1) {
+    if (xl) RowIO<uint16_t, 2>::store((uint16_t*)a.ki_c + orow * a.d_i + 2 * lane, ax);
+  } else if (a.idx_fmt == 2) {
+    if (xl)
+      *reinterpret_cast<uint16_t*>((uint8_t*)a.ki_c + orow * a.d_i + 2 * lane) =
+          (uint16_t)(f32_to_e4m3(ax[0]) | (f32_to_e4m3(ax[1]) << 8));
+  } else {
+    // MXFP4: a 32-element block is one 16-lane group; its amax sets the
+    // e8m0 code floor(log2 amax) - 2 + 127 (0 for an all-zero block)
+    float amax = fmaxf(fabsf(ax[0]), fabsf(ax[1]));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+    int e;
+    frexpf(amax, &e);
+    const int code = amax > 0.f ? min(max(e + 124, 0), 254) : 0;
+    const float x0 = ldexpf(ax[0], 127 - code), x1 = ldexpf(ax[1], 127 - code);
+    if (xl) {
+      ((uint8_t*)a.ki_c)[orow * (a.d_i / 2) + lane] = (uint8_t)(f32_to_e2m1(x0) | (f32_to_e2m1(x1) << 4));
+      if (lane % 16 == 0) a.ki_sc[orow * (a.d_i / 32) + lane / 16] = (uint8_t)code;
+    }
+  }
+}
+
+int launch_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* pos, const void* k_new,
+                        const void* v_new, const float* w_gate, void* k_ring, void* v_ring, void* k_c, void* v_c,
+                        int64_t N_cap, int d_i, int idx_fmt, const void* ki_new, void* ki_ring, void* ki_c,
+                        uint8_t* ki_c_scale, hipStream_t stream) {
+  if (B == 0) return 0;
+  StateArgs a{};
+  a.B = B; a.m = m; a.R = R; a.d_i = d_i; a.idx_fmt = idx_fmt; a.N_cap = N_cap; a.pos = pos;
+  a.k_new = k_new; a.v_new = v_new; a.ki_new = ki_new; a.w_gate = w_gate;
+  a.k_ring = k_ring; a.v_ring = v_ring; a.ki_ring = ki_ring; a.k_c = k_c; a.v_c = v_c; a.ki_c = ki_c;
+  a.ki_sc = ki_c_scale;
+  const dim3 grid((unsigned)((B + kAppendWaves - 1) / kAppendWaves)), block(kAppendWaves * kWave);
+  if (kv_dtype == 0) {
+    if (D == 128) hipLaunchKernelGGL((state_append_kernel<float, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((state_append_kernel<float, 8>), grid, block, 0, stream, a);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((state_append_kernel<uint16_t, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((state_append_kernel<uint16_t, 8>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 int launch_compress(int B, int T_, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,

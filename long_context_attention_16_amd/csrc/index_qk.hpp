@@ -149,7 +149,7 @@ template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() {
 // top-k merge kernel; every entry of the row's top k is in its chunk's top k.
 template <int FMT, int HI, int DI, bool FUSE>
 __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
-    int Lq, int64_t q_pos0, int m, int64_t N_cap, int ngroups, int nchunks,
+    int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
     const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores,
     int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
   const int c = blockIdx.x % nchunks;  // chunk of kIdxColsPerWG entries
   const int gg = blockIdx.x / nchunks;
   const int b = gg / ngroups;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);  // from here on: this sequence's row-0 position
   const int i0 = (gg % ngroups) * G;
   const int nq = min(G, Lq - i0);
   const int64_t n_last = (q_pos0 + i0 + nq) / m;  // visible entries of the group's last query
@@ -367,6 +368,7 @@ struct IdxArgs {
   hipStream_t st;
   int Lq;
   int64_t q_pos0;
+  const int64_t* q_pos;
   int m;
   int64_t N_cap;
   int ngroups, nchunks;
@@ -382,7 +384,7 @@ struct IdxArgs {
 template <int FMT, int HI, int DI, bool FUSE>
 void idx_go(const IdxArgs& a) {
   hipLaunchKernelGGL((index_qk_kernel<FMT, HI, DI, FUSE>), a.grid, dim3(kIdxWaves * kWave), 0, a.st, a.Lq,
-                     a.q_pos0, a.m, a.N_cap, a.ngroups, a.nchunks, a.q, a.qs, a.w, a.k, a.ks, a.sc, a.topk,
+                     a.q_pos0, a.q_pos, a.m, a.N_cap, a.ngroups, a.nchunks, a.q, a.qs, a.w, a.k, a.ks, a.sc, a.topk,
                      a.ck, a.ci);
 }
 
@@ -403,16 +405,16 @@ void idx_dispatch(int H_i, int d_i, const IdxArgs& a) {
 #undef CSA_IDX_D
 }
 
-inline IdxArgs idx_args(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, const void* q_i,
-                        const uint8_t* q_s, const float* w_i, const void* k_i, const uint8_t* k_s,
-                        hipStream_t stream) {
+inline IdxArgs idx_args(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
+                        const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
+                        const uint8_t* k_s, hipStream_t stream) {
   IdxArgs a{};
   const int G = index_qk_queries_per_group(H_i);
   a.ngroups = (Lq + G - 1) / G;
   a.nchunks = index_qk_nchunks(q_pos0, Lq, m);
   a.grid = dim3((unsigned)((int64_t)B * a.ngroups * a.nchunks));
   a.st = stream;
-  a.Lq = Lq; a.q_pos0 = q_pos0; a.m = m; a.N_cap = N_cap;
+  a.Lq = Lq; a.q_pos0 = q_pos0; a.q_pos = q_pos; a.m = m; a.N_cap = N_cap;
   a.q = (const uint8_t*)q_i; a.qs = q_s; a.w = w_i; a.k = (const uint8_t*)k_i; a.ks = k_s;
   return a;
 }

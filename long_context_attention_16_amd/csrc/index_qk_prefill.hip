@@ -73,7 +73,7 @@ __device__ __forceinline__ constexpr int pf_vmcnt(int n) {
 }
 
 __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
-    int Lq, int64_t q_pos0, int m, int64_t N_cap, int ngroups, int nchunks,
+    int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const float* __restrict__ w_i, const uint8_t* __restrict__ k_i,
     float* __restrict__ scores) {
   // Three separate arrays rather than one indexed by block: the compiler
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
   const int c = blockIdx.x % nchunks;
   const int gg = blockIdx.x / nchunks;
   const int b = gg / ngroups;
+  q_pos0 = seq_pos(q_pos, q_pos0, b);  // from here on: this sequence's row-0 position
   const int i0 = (gg % ngroups) * kPfQ;
   const int nq = min(kPfQ, Lq - i0);
   const int64_t n_last = (q_pos0 + i0 + nq) / m;  // visible entries of the group's last query
@@ -262,14 +263,15 @@ bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq) {
   return fmt == 2 && H_i == kPfHeads && d_i == kPfDim && Lq >= kPfQ;
 }
 
-int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const void* q_i,
-                            const float* w_i, const void* k_i, float* scores, hipStream_t stream) {
+int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap,
+                            const void* q_i, const float* w_i, const void* k_i, float* scores,
+                            hipStream_t stream) {
   const int64_t n_max = (q_pos0 + Lq) / m;
   const int nchunks = (int)((n_max + kPfChunk - 1) / kPfChunk);
   const int ngroups = (Lq + kPfQ - 1) / kPfQ;
   if (nchunks == 0 || B == 0 || Lq == 0) return 0;
   const dim3 grid((unsigned)((int64_t)B * ngroups * nchunks));
-  hipLaunchKernelGGL(index_qk_prefill_kernel, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, m, N_cap,
+  hipLaunchKernelGGL(index_qk_prefill_kernel, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, q_pos, m, N_cap,
                      ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

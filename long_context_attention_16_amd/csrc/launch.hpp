@@ -9,7 +9,8 @@ namespace csa {
 // Arguments of the attention kernels (CSA gathered rows and HCA dense rows).
 struct AttnArgs {
   int B, Lq;
-  int64_t q_pos0;
+  int64_t q_pos0;    // position of query row 0, or the bound of q_pos
+  const int64_t* q_pos;  // per-sequence positions of query row 0 [B], or nullptr
   int m;             // HCA block (visible entries n(t) = (t+1)/m)
   int H, D;
   const void* q;
@@ -20,6 +21,7 @@ struct AttnArgs {
   const int32_t* idx;
   int T_raw;
   int64_t raw_pos0;
+  int ring;          // raw rows are a ring of T_raw slots (position s in slot s % T_raw)
   const void* k_raw;
   const void* v_raw;
   int W;
@@ -30,6 +32,18 @@ struct AttnArgs {
   float* ws_ml;      // split (max, sum) [B*Lq][nsplit_max][H][2]
   int nsplit_max;
 };
+
+// Row of absolute position s within a sequence's raw rows (one division per
+// query, for the first window position)...
+__device__ __forceinline__ int64_t attn_raw_row(const AttnArgs& p, int64_t s) {
+  return p.ring ? s % p.T_raw : s - p.raw_pos0;
+}
+// ... and of window row w, from that first row: a window never exceeds the
+// ring, so it wraps at most once.
+__device__ __forceinline__ int64_t attn_window_row(const AttnArgs& p, int64_t row_lo, int w) {
+  const int64_t r = row_lo + w;
+  return p.ring && r >= p.T_raw ? r - p.T_raw : r;
+}
 
 // Rows per split of a query with S sources: S/16 rounded up to a multiple of
 // 32, at least 96 (three 32-row tiles, so each workgroup pipelines loads with
@@ -49,6 +63,11 @@ __host__ __device__ inline int attn_nsplit(int S) {
 int launch_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
                     const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
                     hipStream_t stream);
+// One decode step of the state cache (ring append + completed-block compression).
+int launch_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* pos, const void* k_new,
+                        const void* v_new, const float* w_gate, void* k_ring, void* v_ring, void* k_c, void* v_c,
+                        int64_t N_cap, int d_i, int idx_fmt, const void* ki_new, void* ki_ring, void* ki_c,
+                        uint8_t* ki_c_scale, hipStream_t stream);
 // Query rows scored together by one indexer workgroup (64 / H_i, 1 for H_i = 128).
 int index_qk_queries_per_group(int H_i);
 // Entries per indexer workgroup (the length of a fused candidate source chunk)
@@ -58,12 +77,14 @@ int index_qk_nchunks(int64_t q_pos0, int Lq, int m);
 // Many-query fp8 indexer (64 heads of dim 128, at least 16 query rows per
 // sequence): same scores as launch_index_qk.
 bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq);
-int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const void* q_i,
-                            const float* w_i, const void* k_i, float* scores, hipStream_t stream);
+int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap,
+                            const void* q_i, const float* w_i, const void* k_i, float* scores,
+                            hipStream_t stream);
 // Indexer with the per-chunk top-k fused in (groups of one query only): for
 // each (row, chunk) a list of topk (key, index) pairs at
 // cand_{key,idx}[(row * nchunks + chunk) * topk].
-int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
+int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
+                          int d_i, int fmt,
                           const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
                           const uint8_t* k_s, int topk, uint32_t* cand_key, int32_t* cand_idx,
                           hipStream_t stream);
@@ -77,12 +98,13 @@ size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk);
 bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D);
 size_t attn_decode_ws(int B, int Lq, int H, int topk, int W);
 int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st);
-int launch_index_qk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i, int fmt,
+int launch_index_qk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
+                    int d_i, int fmt,
                     const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
                     const uint8_t* k_s, float* scores, hipStream_t stream);
 size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk);
-int launch_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
-                int32_t* idx_out, void* ws, hipStream_t stream);
+int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, const float* scores,
+                int topk, int32_t* idx_out, void* ws, hipStream_t stream);
 int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t stream);
 
 }  // namespace csa

@@ -30,14 +30,15 @@ constexpr int kTkKeys = kTkThreads * kKPT;     // 32768
 // otherwise the chunk's list of k (key, index), padded with key 0 / index -1.
 template <int KPT>
 __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
-    int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* __restrict__ scores, int topk, int nchunks,
+    int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap,
+    const float* __restrict__ scores, int topk, int nchunks,
     int32_t* __restrict__ final_idx, uint32_t* __restrict__ out_key, int32_t* __restrict__ out_idx) {
   __shared__ TopkShared<kTkThreads, KPT> S;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / nchunks;
   const int chunk = (int)(blockIdx.x % nchunks);
   const int i = (int)(row % Lq);
-  const int n_row = (int)((q_pos0 + i + 1) / m);
+  const int n_row = (int)((seq_pos(q_pos, q_pos0, (int)(row / Lq)) + i + 1) / m);
   const int j0 = chunk * kTkKeys;
   const int n = max(0, min(kTkKeys, n_row - j0));
   int32_t* oi = final_idx ? final_idx + row * topk : out_idx + (row * nchunks + chunk) * topk;
@@ -151,22 +152,22 @@ size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk) {
   return topk_merge_ws_bytes((int64_t)B * Lq, nc, topk);
 }
 
-int launch_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
-                int32_t* idx_out, void* ws, hipStream_t stream) {
+int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, const float* scores,
+                int topk, int32_t* idx_out, void* ws, hipStream_t stream) {
   const int64_t rows = (int64_t)B * Lq;
   if (rows == 0) return 0;
   const int64_t n_max = (q_pos0 + Lq) / m;
   const int nc = max(1, topk_nchunks(n_max));
   const dim3 block(kTkThreads);
   if (nc == 1) {
-    CSA_TOPK_KPT(kpt_for(n_max), topk_chunk_kernel, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, m, N_cap,
-                 scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr);
+    CSA_TOPK_KPT(kpt_for(n_max), topk_chunk_kernel, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m,
+                 N_cap, scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr);
     return hipGetLastError() == hipSuccess ? 0 : 1;
   }
   uint32_t* k0 = (uint32_t*)ws;
   int32_t* i0 = (int32_t*)(k0 + rows * nc * topk);
-  hipLaunchKernelGGL(topk_chunk_kernel<kKPT>, dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0, m, N_cap,
-                     scores, topk, nc, (int32_t*)nullptr, k0, i0);
+  hipLaunchKernelGGL(topk_chunk_kernel<kKPT>, dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0, q_pos,
+                     m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
   if (hipGetLastError() != hipSuccess) return 1;
   return launch_topk_merge(rows, nc, topk, ws, idx_out, stream);
 }

@@ -29,14 +29,14 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 19, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
 
 
 def test_version_and_strerror(lib):
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     for code in range(7):
         assert len(lib.csa_strerror(code)) > 0
     assert lib.csa_strerror(99) == b"unknown status"
@@ -143,3 +143,41 @@ def test_attention_rejects(lib):
     assert g(*hb[:8], 6, *hb[9:]) == SHAPE        # n(1000) = 7 entries need N_cap >= 7
     bad = list(hb); bad[6] = 3
     assert g(*bad) == DTYPE
+
+
+def test_state_and_varlen_reject(lib):
+    f = lib.csa_state_append
+    base = [4, 512, 4, 128, 1, P, P, P, P, P, P, P, P, 64, 128, 2, P, P, P, None, None]
+    assert f(*base[:5], None, *base[6:]) == NULL          # positions
+    bad = list(base); bad[3] = 3
+    assert f(*bad) == SHAPE                               # ring smaller than a block
+    bad = list(base); bad[14] = 48
+    assert f(*bad) == SHAPE                               # indexer dim
+    bad = list(base); bad[15] = 3
+    assert f(*bad) == NULL                                # fp4 keys need scales
+    bad = list(base); bad[16] = None
+    assert f(*bad) == NULL                                # indexer key rows
+    bad = list(base); bad[4] = 2
+    assert f(*bad) == DTYPE
+    bad = list(base); bad[5] = P + 4
+    assert f(*bad) == ALIGN                               # int64 positions
+    nb = list(base); nb[14] = 0; nb[16] = nb[17] = nb[18] = None
+    bad = list(nb); bad[1] = 96
+    assert f(*bad) == SHAPE                               # D
+    g = lib.csa_index_topk_varlen
+    n = lib.csa_index_topk_ws_bytes(2, 1, 200, 4, 64, 8)
+    vb = [2, 1, P, 200, 4, 64, 4, 32, 1, P, None, P, P, None, 8, P, P, n, None]
+    assert g(*vb[:2], None, *vb[3:]) == NULL
+    bad = list(vb); bad[5] = 49
+    assert g(*bad) == SHAPE                               # n(200) = 50 entries need N_cap >= 50
+    a = lib.csa_sparse_attn_varlen
+    na = lib.csa_sparse_attn_ws_bytes(2, 1, 4, 128, 16, 8)
+    ab = [2, 1, P, 100, 4, 128, 1, P, 64, P, P, 16, P, 8, P, P, 8, None, P, None, P, na, None]
+    assert a(*ab[:2], None, *ab[3:]) == NULL
+    bad = list(ab); bad[13] = 7
+    assert a(*bad) == SHAPE                               # W = 8 rows need a ring of 8
+    h = lib.hca_dense_attn_varlen
+    nh = lib.hca_dense_attn_ws_bytes(2, 1, 1000, 128, 4, 128, 8)
+    hb = [2, 1, P, 1000, 128, 4, 128, 1, P, 6, P, P, 8, P, P, 8, None, P, None, P, nh, None]
+    assert h(*hb) == SHAPE                                # n(1000) = 7 entries need N_cap >= 7
+    assert h(*hb[:2], None, *hb[3:]) == NULL
