@@ -10,9 +10,12 @@ HBM. Two independent input sets alternate between steps so the working set is
 larger than the 256 MB Infinity Cache.
 
 Other workloads (--workload): hca_decode (HCA at 1M context, batch 16),
-pair_1m (CSA with an MXFP4 indexer plus HCA at 1M context, batch 8) and
+pair_1m (CSA with an MXFP4 indexer plus HCA at 1M context, batch 8),
 indexer_fp8_prefill (the fp8 indexer of a 4096-token prefill chunk at 64K
-context with 64 heads x 128 dims).
+context with 64 heads x 128 dims), compress (the compressor's bandwidth) and
+csa_decode_state (the CSA decode step with the state cache: token append and
+block compression, then indexer top-k and attention with a position per
+sequence around 128K).
 
 Prints one JSON line. The CPU baseline times the CPU oracle (test
 infrastructure) on a bounded sample of the same workload on the host cores.
@@ -37,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode",
-                    choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress"])
+                    choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress",
+                             "csa_decode_state"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB copy (calibration run for HBM byte counters)")
@@ -227,6 +231,105 @@ def bench_compress(args, torch, csa, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_state_decode(args, torch, csa, wl, dev):
+    """The CSA decode step with the state cache at 128K context, batch 32:
+    csa_state_append (each token into its sequence's 128-slot ring; the
+    sequences whose token completes a block of 4 compress it, a quarter of the
+    batch per step), then csa_index_topk_varlen and csa_sparse_attn_varlen
+    with one position per sequence (131071 - 37 b: lengths differ, and
+    b % 4 == 0 completes a block). HIP-graph replays of the whole step, two
+    input sets alternating."""
+    s = wl.CFG2
+    R, d_i = s.T_raw, s.d_I
+    pos_l = [s.q_pos0 - 37 * b for b in range(s.B)]
+    q_pos_max = max(pos_l)
+    sets = []
+    for sd in (wl.SEEDS["2"], 1000 + wl.SEEDS["2"]):
+        x = wl.make_inputs(s, sd, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(sd + 5)
+        bf = lambda *sh: torch.randn(sh, generator=gen, device=dev).to(torch.bfloat16)
+        x.update(pos=torch.tensor(pos_l, dtype=torch.int64, device=dev), k_new=bf(s.B, s.D), v_new=bf(s.B, s.D),
+                 ki_new=bf(s.B, d_i), ki_ring=bf(s.B, R, d_i),
+                 idx=torch.empty((s.B, 1, s.topk), dtype=torch.int32, device=dev),
+                 out=torch.empty_like(x["q"]), lse=torch.empty((s.B, 1, s.H), dtype=torch.float32, device=dev))
+        ib = csa.index_topk_ws_bytes(s.B, 1, q_pos_max, s.m, s.N_cap, s.topk)
+        x["iws"] = torch.empty((ib + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        ab = csa.sparse_attn_ws_bytes(s.B, 1, s.H, s.D, s.topk, s.W)
+        x["aws"] = torch.empty((ab + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        sets.append(x)
+    torch.cuda.synchronize()
+
+    def launch(label, x):
+        if label == "state_append":
+            csa.state_append(x["pos"], x["k_new"], x["v_new"], x["w_gate"], s.m, x["k_raw"], x["v_raw"], x["k_c"],
+                             x["v_c"], x["ki_new"], x["ki_ring"], x["k_i"], None, s.idx)
+        elif label == "index_topk":
+            csa.index_topk_varlen(x["q_i"], x["w_i"], x["k_i"], s.topk, x["pos"], q_pos_max, s.m, s.idx,
+                                  ws=x["iws"], out=x["idx"])
+        else:
+            csa.sparse_attn_varlen(x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"], s.W, x["sink"],
+                                   x["pos"], q_pos_max, ws=x["aws"], out=x["out"], lse=x["lse"])
+
+    labels = ["state_append", "index_topk", "sparse_attn"]
+    for k in range(args.warmup):
+        for l in labels:
+            launch(l, sets[k % 2])
+    torch.cuda.synchronize()
+    breakdown = {}
+    for l in labels:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(args.steps):
+            launch(l, sets[k % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        breakdown[l] = round(1000.0 * e0.elapsed_time(e1) / args.steps, 2)
+    graphs = []
+    for k in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in labels:
+                launch(l, sets[k])
+        graphs.append(g)
+    for k in range(args.warmup):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+
+    # algorithmic bytes of the index_topk call: the visible k_I rows of each
+    # sequence, q_I and head weights, the candidate lists written and read,
+    # the indices written
+    vis = [(p + 1) // s.m for p in pos_l]
+    nch = (max(vis) + 2047) // 2048
+    row = idx_row_bytes(s)
+    ib = sum(vis) * row + s.B * s.H_I * (row + 4) + 2 * s.B * nch * s.topk * 8 + s.B * s.topk * 4
+    roof = {"bound": "hbm", "achieved": ib / (breakdown["index_topk"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update(traffic=None, kernel="index_topk (fused indexer + merge)", bytes_per_launch=ib)
+    roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
+    result = {
+        "metric": "CSA decode query-tok/s with state cache @128K ctx", "value": round(s.B / (ms / 1000.0), 1),
+        "unit": "query-tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) caches, tokens and queries, random-init indexer; no weights or datasets)",
+        "config": {"workload": "csa_decode_state_128k_b32_bf16", "batch": s.B,
+                   "positions": "131071 - 37 b", "ring_slots": R, "m": s.m, "compressing_per_step": sum(
+                       1 for p in pos_l if (p + 1) % s.m == 0), "heads": s.H, "head_dim": s.D,
+                   "indexer": "%dx%d %s" % (s.H_I, s.d_I, s.idx), "topk": s.topk, "window": s.W},
+        "roofline": roof, "breakdown_us": breakdown,
+        "timing": "value/ms_per_step: HIP-graph replays of the whole step; breakdown_us: back-to-back calls "
+                  "between HIP events",
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
@@ -342,6 +445,9 @@ def main():
     W = args.workload
     if W == "compress":
         bench_compress(args, torch, csa, dev)
+        return
+    if W == "csa_decode_state":
+        bench_state_decode(args, torch, csa, wl, dev)
         return
     if W == "csa_decode":
         shapes = [("", wl.CFG2)]

@@ -353,13 +353,15 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void state_append_kernel(Stat
     ax[1] = fmaf(ax[1], scale, p * xv[1]);
     run_max = nmax;
   };
-  // rows t - m + 1 .. t - 1 from the ring (slots wrap once at most per row
-  // step), four loaded before the first of them is folded; then the new row
+  // rows t - m + 1 .. t - 1 from the ring in batches of four, all four
+  // loaded before the first is folded (one round trip for m = 4); the rows of
+  // a batch past the block read a valid slot and are not folded. Then the
+  // new row.
   int64_t slot = (t - m + 1) % a.R;
   auto next = [&](int64_t sl) { return sl + 1 == a.R ? (int64_t)0 : sl + 1; };
   constexpr int kAhead = 4;
-  int s = 0;
-  for (; s + kAhead <= m - 1; s += kAhead) {
+  for (int s = 0; s < m - 1; s += kAhead) {
+    const int cnt = min(kAhead, m - 1 - s);
     float kv[kAhead][VEC], vv[kAhead][VEC], xv[kAhead][2];
 #pragma unroll
     for (int u = 0; u < kAhead; ++u) {
@@ -370,15 +372,8 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void state_append_kernel(Stat
       slot = next(slot);
     }
 #pragma unroll
-    for (int u = 0; u < kAhead; ++u) fold(kv[u], vv[u], xv[u]);
-  }
-  for (; s < m - 1; ++s) {
-    float kv[VEC], vv[VEC], xv[2] = {0.f, 0.f};
-    RowIO<T, VEC>::load(kr + slot * D, kv);
-    RowIO<T, VEC>::load(vr + slot * D, vv);
-    if (xl) RowIO<T, 2>::load(xr + slot * a.d_i, xv);
-    slot = next(slot);
-    fold(kv, vv, xv);
+    for (int u = 0; u < kAhead; ++u)
+      if (u < cnt) fold(kv[u], vv[u], xv[u]);
   }
   fold(kn, vn, xn);
   const float inv = 1.0f / run_sum;
