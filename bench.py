@@ -327,6 +327,9 @@ def bench_state_decode(args, torch, csa, wl, dev):
                   "between HIP events",
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline("csa_decode_state_128k_b32_bf16", [(s, sets[0])], args.cpu_seconds,
+                                              query_fn=lambda s_, x_, b_: _oracle_state_query(s_, x_, b_, pos_l[b_]))
     print(json.dumps(result), flush=True)
 
 
@@ -392,7 +395,45 @@ def _oracle_query(s, x, b):
     return spent
 
 
-def cpu_baseline(wl_name, parts, seconds):
+def _oracle_state_query(s, x, b, t):
+    """Oracle seconds for one decode step of sequence b at position t with the
+    state cache: the token enters the ring and, when it completes a block, the
+    block is compressed (the oracle's state-cache steps), then indexer,
+    top-k and attention with the window read from the ring. Copying the rows
+    it reads from the GPU is not timed."""
+    import numpy as np
+    import torch
+    from oracle import attention as oatt, compress as ocmp, formats, indexer as oidx, topk as otopk
+
+    def bf(t_):
+        return formats.bf16_to_f64(t_.view(torch.int16).numpy().view(np.uint16))
+
+    R = x["k_raw"].shape[1]
+    n = (t + 1) // s.m
+    kr, vr, xr = x["k_raw"][b].cpu(), x["v_raw"][b].cpu(), x["ki_ring"][b].cpu()
+    kn, vn, xn = x["k_new"][b].cpu(), x["v_new"][b].cpu(), x["ki_new"][b].cpu()
+    w_gate = x["w_gate"].cpu().numpy().astype(np.float64)
+    qi, wi, ki = x["q_i"][b].cpu(), x["w_i"][b].cpu(), x["k_i"][b][:n].cpu()
+    q, sink = x["q"][b].cpu(), x["sink"].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    K, V, X = bf(kr), bf(vr), bf(xr)
+    K[t % R], V[t % R], X[t % R] = bf(kn), bf(vn), bf(xn)
+    if (t + 1) % s.m == 0:
+        blk = np.arange(t - s.m + 1, t + 1) % R
+        ocmp.compress(K[blk], V[blk], w_gate, s.m, pos0=t - s.m + 1, x_raw=X[blk])
+    sc = oidx.index_scores(bf(qi[0]), wi[0].numpy().astype(np.float64), bf(ki))
+    sel = otopk.topk_select(sc, s.topk)
+    sel = sel[sel >= 0]
+    spent = time.perf_counter() - t0
+    rows = torch.from_numpy(sel).to(x["k_c"].device)
+    kc, vc = x["k_c"][b][rows].cpu(), x["v_c"][b][rows].cpu()
+    t0 = time.perf_counter()
+    pos = np.arange(max(0, t - s.W + 1), t + 1)
+    oatt.attend_one(bf(q[0]), t, bf(kc), bf(vc), K[pos % R], pos, V[pos % R], sink)
+    return spent + time.perf_counter() - t0
+
+
+def cpu_baseline(wl_name, parts, seconds, query_fn=None):
     """Time the CPU oracle, as it stands, on whole query tokens of the same
     workload (every layer of it) until `seconds` of oracle work have run."""
     try:
@@ -405,7 +446,7 @@ def cpu_baseline(wl_name, parts, seconds):
     done, spent = 0, 0.0
     while done < B and (done == 0 or spent < seconds):
         for s, x in parts:
-            spent += _oracle_query(s, x, done)
+            spent += query_fn(s, x, done) if query_fn else _oracle_query(s, x, done)
         done += 1
     cpu = platform.processor() or ""
     try:
