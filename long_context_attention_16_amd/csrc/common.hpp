@@ -88,13 +88,6 @@ __device__ __forceinline__ void rope_cos_sin(int64_t p, int i, float* c, float* 
   rope_cos_sin_f(p, kRopeRev[i], c, s);
 }
 
-// ---------------------------------------------------------------- top-k keys
-// Order-preserving map of a finite float to uint32 (larger float -> larger
-// key); -0 and +0 map to the same key.
-// max(x, 0) as one integer max on the bit pattern: a float's sign bit makes
-// every negative value (and -0) a negative int32, so they become +0 and
-// everything else passes unchanged. fmaxf on a value the compiler cannot
-// prove quiet costs an extra canonicalizing max in IEEE mode.
 // Absolute position of query row 0 of sequence b: `bound` for every
 // sequence, or q_pos[b] clamped into [0, bound] when per-sequence positions
 // are given (q_pos != nullptr; bound is then their upper bound, which sized
@@ -105,11 +98,18 @@ __device__ __forceinline__ int64_t seq_pos(const int64_t* q_pos, int64_t bound, 
   return v < 0 ? 0 : (v > bound ? bound : v);
 }
 
+// max(x, 0) as one integer max on the bit pattern: a float's sign bit makes
+// every negative value (and -0) a negative int32, so they become +0 and
+// everything else passes unchanged. fmaxf on a value the compiler cannot
+// prove quiet costs an extra canonicalizing max in IEEE mode.
 __device__ __forceinline__ float relu_bits(float x) {
   const int v = __builtin_bit_cast(int, x);
   return __builtin_bit_cast(float, v > 0 ? v : 0);
 }
 
+// ---------------------------------------------------------------- top-k keys
+// Order-preserving map of a finite float to uint32 (larger float -> larger
+// key); -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7FFFFFFFu) == 0) return 0x80000000u;
