@@ -45,6 +45,8 @@ SIGNATURES = {
                                     _P, _P, _P, _P, _Z, _P]),
     "hca_dense_attn_varlen": (_I, [_I, _I, _P, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _P, _P, _I,
                                    _P, _P, _P, _P, _Z, _P]),
+    "csa_index_topk_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
+                               _Z, _P]),
 }
 
 _lib = None
@@ -308,3 +310,22 @@ def hca_attn_varlen(q, k_c, v_c, m, k_ring, v_ring, W, sink, q_pos, q_pos_max, w
                                        _ptr(v_ring), W, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream()))
     return out, lse
+
+
+def index_topk_ex(q_i, w_i, k_i, topk, q_pos0, m, fmt, score_dtype="bf16", q_pos=None, q_scale=None,
+                  k_scale=None, ws=None, out=None):
+    """index_topk with the score precision ('f32' or 'bf16': scores rounded
+    to bfloat16 before the top-k) and optional per-sequence positions q_pos
+    [B] int64 (then q_pos0 is their bound)."""
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if ws is None:
+        ws = _ws(index_topk_ws_bytes(B, Lq, q_pos0, m, N_cap, topk), q_i.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk), dtype=torch.int32, device=q_i.device)
+    _check(lib().csa_index_topk_ex(B, Lq, None if q_pos is None else _pos_tensor(q_pos), q_pos0, m, N_cap, H_i,
+                                   d_i, IDX_FORMATS[fmt], _ptr(q_i), _ptr(q_scale), _ptr(w_i), _ptr(k_i),
+                                   _ptr(k_scale), topk, IDX_FORMATS[score_dtype], _ptr(out), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream()))
+    return out

@@ -115,12 +115,13 @@ static bool use_fused(int Lq, int H_i, int topk) {
 
 static int launch_candidates(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                              int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
-                             const void* k_i, const uint8_t* k_i_scale, int topk, void* cand, hipStream_t st) {
+                             const void* k_i, const uint8_t* k_i_scale, int topk, int sbf, void* cand,
+                             hipStream_t st) {
   const int64_t rows = (int64_t)B * Lq;
   uint32_t* ck = (uint32_t*)cand;
   int32_t* ci = (int32_t*)(ck + rows * index_qk_nchunks(q_pos0, Lq, m) * topk);
   return launch_index_qk_fused(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
-                               k_i_scale, topk, ck, ci, st);
+                               k_i_scale, topk, sbf, ck, ci, st);
 }
 
 size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk) {
@@ -160,14 +161,15 @@ int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_
     return rc;
   if (!aligned16(scores)) return CSA_ERR_ALIGN;
   return launch_index_qk(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
-                         k_i_scale, scores, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+                         k_i_scale, scores, 0, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
-// csa_index_topk and csa_index_topk_varlen: q_pos == nullptr means every
-// sequence's row 0 is at q_pos0; otherwise q_pos0 bounds the q_pos values.
+// csa_index_topk, csa_index_topk_varlen and csa_index_topk_ex: q_pos ==
+// nullptr means every sequence's row 0 is at q_pos0; otherwise q_pos0 bounds
+// the q_pos values. sbf: scores rounded to bf16 before the top-k.
 static int index_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                       int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
-                      const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
+                      const void* k_i, const uint8_t* k_i_scale, int topk, int sbf, int32_t* idx_out, void* ws,
                       size_t ws_bytes, void* stream) {
   if (!idx_out) return CSA_ERR_NULL;
   if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
@@ -179,7 +181,7 @@ static int index_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m
   hipStream_t st = as_stream(stream);
   if (use_fused(Lq, H_i, topk)) {
     if (launch_candidates(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
-                          k_i_scale, topk, ws, st))
+                          k_i_scale, topk, sbf, ws, st))
       return CSA_ERR_LAUNCH;
     return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, ws, idx_out, st)
                ? CSA_ERR_LAUNCH : CSA_OK;
@@ -187,9 +189,10 @@ static int index_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m
   float* scores = (float*)ws;
   void* cand = (char*)ws + scores_bytes(B, Lq, N_cap);
   if (launch_index_qk(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
-                      k_i_scale, scores, st))
+                      k_i_scale, scores, sbf, st))
     return CSA_ERR_LAUNCH;
-  return launch_topk(B, Lq, q_pos0, q_pos, m, N_cap, scores, topk, idx_out, cand, st) ? CSA_ERR_LAUNCH : CSA_OK;
+  return launch_topk(B, Lq, q_pos0, q_pos, m, N_cap, scores, sbf, topk, idx_out, cand, st) ? CSA_ERR_LAUNCH
+                                                                                          : CSA_OK;
 }
 
 int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
@@ -197,7 +200,7 @@ int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_i,
                    const void* k_i, const uint8_t* k_i_scale, int topk, int32_t* idx_out, void* ws,
                    size_t ws_bytes, void* stream) {
   return index_topk(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
-                    topk, idx_out, ws, ws_bytes, stream);
+                    topk, 0, idx_out, ws, ws_bytes, stream);
 }
 
 int csa_index_topk_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max, int m, int64_t N_cap,
@@ -206,7 +209,16 @@ int csa_index_topk_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max
                           int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
   if (!q_pos) return CSA_ERR_NULL;
   return index_topk(B, Lq, q_pos_max, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
-                    topk, idx_out, ws, ws_bytes, stream);
+                    topk, 0, idx_out, ws, ws_bytes, stream);
+}
+
+int csa_index_topk_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int m, int64_t N_cap, int H_i, int d_i,
+                      int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i, const void* k_i,
+                      const uint8_t* k_i_scale, int topk, int score_dtype, int32_t* idx_out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) return CSA_ERR_DTYPE;
+  return index_topk(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i, k_i_scale,
+                    topk, score_dtype == CSA_BF16, idx_out, ws, ws_bytes, stream);
 }
 
 int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* scores, int topk,
@@ -215,7 +227,7 @@ int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* s
   if (int rc = check_topk_shape(B, Lq, q_pos0, m, N_cap, topk)) return rc;
   if (!aligned16(scores) || !aligned16(idx_out) || !aligned16(ws)) return CSA_ERR_ALIGN;
   if (!ws || ws_bytes < csa_topk_ws_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
-  return launch_topk(B, Lq, q_pos0, nullptr, m, N_cap, scores, topk, idx_out, ws, as_stream(stream))
+  return launch_topk(B, Lq, q_pos0, nullptr, m, N_cap, scores, 0, topk, idx_out, ws, as_stream(stream))
              ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
@@ -237,7 +249,7 @@ int csa_index_candidates(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, in
   if (cand_bytes < csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
   return launch_candidates(B, Lq, q_pos0, nullptr, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
-                           k_i_scale, topk, cand, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+                           k_i_scale, topk, 0, cand, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, size_t cand_bytes,

@@ -116,4 +116,27 @@ __device__ __forceinline__ uint32_t score_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Key of a score rounded to bfloat16 (nearest even), as a 32-bit key whose
+// low 16 bits are zero: `key >> 16` orders the same way, so a selection can
+// run on 16-bit keys and hand on `key16 << 16`.
+__device__ __forceinline__ uint32_t score_key_bf16(float f) {
+  return score_key(bf16_bits_to_f32(f32_to_bf16_bits(f))) & 0xFFFF0000u;
+}
+
+// Row stride, in elements, of a score matrix: N_cap for f32; for bf16 N_cap
+// rounded up to even, so a 4-byte store of two neighbouring entries never
+// crosses into the next row.
+__host__ __device__ inline int64_t score_stride(int64_t N_cap, int sbf) { return sbf ? (N_cap + 1) & ~(int64_t)1 : N_cap; }
+
+// 32-bit word a lane stores for its score v: the f32 bits, or for bf16 scores
+// the pair (its entry, the next lane's entry), which the even lane of each
+// pair stores (lanes 2i and 2i+1 hold neighbouring entries of one row). The
+// lanes swap values with one DPP move (quad_perm [1,0,3,2]); every lane
+// executes it.
+__device__ __forceinline__ uint32_t score_word(float v, int sbf) {
+  const int nb = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false);
+  return sbf ? ((uint32_t)f32_to_bf16_bits(v) | ((uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, nb)) << 16))
+             : __builtin_bit_cast(uint32_t, v);
+}
+
 }  // namespace csa

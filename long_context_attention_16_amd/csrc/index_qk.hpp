@@ -151,7 +151,7 @@ template <int FMT, int HI, int DI, bool FUSE>
 __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
-    const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores,
+    const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores, int sbf,
     int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
   constexpr int MTILES = HI == 128 ? 4 : 2;
   constexpr int G = MTILES * 32 / HI;  // queries per group
@@ -258,21 +258,28 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
   // built from wave-uniform values, read as scalars (built from a
   // min<int64_t>, it would be taken as divergent and every store wrapped in a
   // loop over lanes). Fused: an LDS store, masked lanes writing a dump row.
-  const uint64_t sbase = FUSE ? 0 : (uint64_t)(scores + ((int64_t)b * Lq + i0) * N_cap);
+  // bf16 scores (sbf): rows of score_stride(N_cap, 1) entries, each lane pair
+  // stored as one word by its even lane (score_word), so every lane still
+  // issues exactly one store per put.
+  const int esz = sbf ? 2 : 4;
+  const int64_t sstride = score_stride(N_cap, sbf);
+  const uint64_t sbase = FUSE ? 0 : (uint64_t)((uint8_t*)scores + ((int64_t)b * Lq + i0) * sstride * esz);
   const uint32_t slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   const uint32_t shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
-  const int snum = __builtin_amdgcn_readfirstlane((int)((int64_t)nq * N_cap * 4));
+  const int snum = __builtin_amdgcn_readfirstlane((int)((int64_t)nq * sstride * esz));
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(((uint64_t)shi << 32) | slo), 0, snum, 0x00020000);
   constexpr int kDrop = 0x7FFFFFF0;
-  const uint32_t ncap4 = (uint32_t)N_cap * 4u;
+  const uint32_t srow = (uint32_t)(sstride * esz);
+  const bool s_lane = !sbf || (lane & 1) == 0;  // lanes that store
   const int col0 = tile0 * 32;
   auto put = [&](int qq, int jrel, bool ok, float v) {
     if constexpr (FUSE) {
       s_sc[ok ? jrel - col0 : kIdxColsPerWG + lane] = v;  // one query: qq == 0 whenever ok
     } else {
-      const int off = ok ? (int)((uint32_t)qq * ncap4 + (uint32_t)jrel * 4u) : kDrop;
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), srsrc, off, 0, 0);
+      const uint32_t word = score_word(v, sbf);
+      const int off = ok && s_lane ? (int)((uint32_t)qq * srow + (uint32_t)jrel * (uint32_t)esz) : kDrop;
+      __builtin_amdgcn_raw_buffer_store_b32(word, srsrc, off, 0, 0);
     }
   };
 
@@ -344,19 +351,22 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
     const int64_t o = (((int64_t)b * Lq + i0) * nchunks + c) * topk;
     uint32_t* ok = cand_key + o;
     int32_t* oi = cand_idx + o;
+    // bf16 scores: keys of the rounded scores, selected as 16-bit keys
+    auto keyof = [&](float x) { return sbf ? score_key_bf16(x) : score_key(x); };
+    const int ksh = sbf ? 16 : 0;
     if (n <= topk) {  // every visible entry of the chunk is a candidate
       for (int p = threadIdx.x; p < topk; p += kSelThreads) {
         const bool v = p < n;
-        ok[p] = v ? score_key(s_sc[p]) : 0u;
+        ok[p] = v ? keyof(s_sc[p]) : 0u;
         oi[p] = v ? col0 + p : -1;
       }
       return;
     }
     uint32_t key[kSelKPT];
 #pragma unroll
-    for (int u = 0; u < kSelKPT; ++u) key[u] = score_key(s_sc[min(u * kSelThreads + (int)threadIdx.x, n - 1)]);
+    for (int u = 0; u < kSelKPT; ++u) key[u] = keyof(s_sc[min(u * kSelThreads + (int)threadIdx.x, n - 1)]) >> ksh;
     block_select<kSelThreads, kSelKPT>(key, n, topk, s_sel, [&](int slot, int u) {
-      ok[slot] = key[u];
+      ok[slot] = key[u] << ksh;
       oi[slot] = col0 + u * kSelThreads + (int)threadIdx.x;
     });
   }
@@ -376,6 +386,7 @@ struct IdxArgs {
   const float* w;
   const uint8_t *k, *ks;
   float* sc;
+  int sbf;
   int topk;
   uint32_t* ck;
   int32_t* ci;
@@ -384,7 +395,7 @@ struct IdxArgs {
 template <int FMT, int HI, int DI, bool FUSE>
 void idx_go(const IdxArgs& a) {
   hipLaunchKernelGGL((index_qk_kernel<FMT, HI, DI, FUSE>), a.grid, dim3(kIdxWaves * kWave), 0, a.st, a.Lq,
-                     a.q_pos0, a.q_pos, a.m, a.N_cap, a.ngroups, a.nchunks, a.q, a.qs, a.w, a.k, a.ks, a.sc, a.topk,
+                     a.q_pos0, a.q_pos, a.m, a.N_cap, a.ngroups, a.nchunks, a.q, a.qs, a.w, a.k, a.ks, a.sc, a.sbf, a.topk,
                      a.ck, a.ci);
 }
 

@@ -7,11 +7,11 @@ namespace csa {
 int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                           int d_i, int fmt,
                           const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
-                          const uint8_t* k_s, int topk, uint32_t* cand_key, int32_t* cand_idx,
+                          const uint8_t* k_s, int topk, int sbf, uint32_t* cand_key, int32_t* cand_idx,
                           hipStream_t stream) {
   if (index_qk_nchunks(q_pos0, Lq, m) == 0 || B == 0 || Lq == 0) return 0;
   IdxArgs a = idx_args(B, Lq, q_pos0, q_pos, m, N_cap, H_i, q_i, q_s, w_i, k_i, k_s, stream);
-  a.topk = topk; a.ck = cand_key; a.ci = cand_idx;
+  a.topk = topk; a.sbf = sbf; a.ck = cand_key; a.ci = cand_idx;
   switch (fmt) {
     case 0: idx_dispatch<0, true>(H_i, d_i, a); break;
     case 1: idx_dispatch<1, true>(H_i, d_i, a); break;

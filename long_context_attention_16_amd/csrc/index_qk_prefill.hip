@@ -75,7 +75,7 @@ __device__ __forceinline__ constexpr int pf_vmcnt(int n) {
 __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const float* __restrict__ w_i, const uint8_t* __restrict__ k_i,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, int sbf) {
   // Three separate arrays rather than one indexed by block: the compiler
   // then knows which ring buffer an LDS read touches and waits only for the
   // copies into that buffer, not for the blocks still in flight.
@@ -162,13 +162,18 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
 
   // Score stores relative to (row i0 + 2*wave, entry j0); the lane's row is
   // that + half. Offsets past the resource's end are dropped.
-  const uint64_t sbase = (uint64_t)(scores + ((int64_t)b * Lq + i0 + 2 * wave) * N_cap + j0);
+  // bf16 scores (sbf): rows of score_stride(N_cap, 1) entries, each lane
+  // pair's word stored by its even lane; every lane still issues one store.
+  const int esz = sbf ? 2 : 4;
+  const int64_t sstride = score_stride(N_cap, sbf);
+  const uint64_t sbase = (uint64_t)((uint8_t*)scores + (((int64_t)b * Lq + i0 + 2 * wave) * sstride + j0) * esz);
   const uint32_t slo = __builtin_amdgcn_readfirstlane((uint32_t)sbase);
   const uint32_t shi = __builtin_amdgcn_readfirstlane((uint32_t)(sbase >> 32));
   const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(((uint64_t)shi << 32) | slo), 0, (int)(N_cap * 4 + kPfChunk * 4), 0x00020000);
+      (void*)(((uint64_t)shi << 32) | slo), 0, (int)((sstride + kPfChunk) * esz), 0x00020000);
   constexpr int kDrop = 0x7FFFFFF0;
-  const int row_off = half ? (int)(N_cap * 4) : 0;
+  const int row_off = half ? (int)(sstride * esz) : 0;
+  const bool s_lane = !sbf || (lane & 1) == 0;
 
   // B fragments of step st of an LDS block (two k-steps, entries 32st..+31).
   auto frags = [&](const uint8_t* kt, int st, i32x8 (&kf)[2]) {
@@ -202,8 +207,9 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
       for (int e = 0; e < 16; ++e) p[e % 4] = fmaf(wr[mt][e], relu_bits(acc[mt][e]), p[e % 4]);
     const float tot = (p[0] + p[1]) + (p[2] + p[3]);
     const int jrel = g * 32 + n32;
-    const int off = (uint32_t)jrel < ulim ? row_off + jrel * 4 : kDrop;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, tot), srsrc, off, 0, 0);
+    const uint32_t word = score_word(tot, sbf);
+    const int off = (uint32_t)jrel < ulim && s_lane ? row_off + jrel * esz : kDrop;
+    __builtin_amdgcn_raw_buffer_store_b32(word, srsrc, off, 0, 0);
   };
 
   // Step order: MFMAs of step g, LDS reads of step g+1 into the same
@@ -264,7 +270,7 @@ bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq) {
 }
 
 int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap,
-                            const void* q_i, const float* w_i, const void* k_i, float* scores,
+                            const void* q_i, const float* w_i, const void* k_i, float* scores, int sbf,
                             hipStream_t stream) {
   const int64_t n_max = (q_pos0 + Lq) / m;
   const int nchunks = (int)((n_max + kPfChunk - 1) / kPfChunk);
@@ -272,7 +278,7 @@ int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos,
   if (nchunks == 0 || B == 0 || Lq == 0) return 0;
   const dim3 grid((unsigned)((int64_t)B * ngroups * nchunks));
   hipLaunchKernelGGL(index_qk_prefill_kernel, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, q_pos, m, N_cap,
-                     ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores);
+                     ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores, sbf);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

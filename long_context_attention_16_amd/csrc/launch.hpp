@@ -78,15 +78,17 @@ int index_qk_nchunks(int64_t q_pos0, int Lq, int m);
 // sequence): same scores as launch_index_qk.
 bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq);
 int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap,
-                            const void* q_i, const float* w_i, const void* k_i, float* scores,
+                            const void* q_i, const float* w_i, const void* k_i, float* scores, int sbf,
                             hipStream_t stream);
+// sbf != 0: scores in bfloat16 (rows of score_stride(N_cap, 1) entries) and
+// the top-k ordered by the rounded scores.
 // Indexer with the per-chunk top-k fused in (groups of one query only): for
 // each (row, chunk) a list of topk (key, index) pairs at
 // cand_{key,idx}[(row * nchunks + chunk) * topk].
 int launch_index_qk_fused(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                           int d_i, int fmt,
                           const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
-                          const uint8_t* k_s, int topk, uint32_t* cand_key, int32_t* cand_idx,
+                          const uint8_t* k_s, int topk, int sbf, uint32_t* cand_key, int32_t* cand_idx,
                           hipStream_t stream);
 // Merge levels over nlists candidate lists of topk per row (rows = B * Lq),
 // then the final indices; ws holds the lists at level 0 and room for level 1.
@@ -101,10 +103,10 @@ int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st);
 int launch_index_qk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                     int d_i, int fmt,
                     const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
-                    const uint8_t* k_s, float* scores, hipStream_t stream);
+                    const uint8_t* k_s, float* scores, int sbf, hipStream_t stream);
 size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk);
 int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, const float* scores,
-                int topk, int32_t* idx_out, void* ws, hipStream_t stream);
+                int sbf, int topk, int32_t* idx_out, void* ws, hipStream_t stream);
 int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t stream);
 
 }  // namespace csa

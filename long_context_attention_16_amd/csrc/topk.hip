@@ -28,7 +28,9 @@ constexpr int kTkKeys = kTkThreads * kKPT;     // 32768
 // Chunk level: workgroup = (row, chunk of 32768 entries). final_idx !=
 // nullptr: the row fits one chunk and the final indices are written;
 // otherwise the chunk's list of k (key, index), padded with key 0 / index -1.
-template <int KPT>
+// SBF: bf16 scores in rows of score_stride(N_cap, 1) entries, selected on
+// 16-bit keys (score_key_bf16 >> 16).
+template <int KPT, bool SBF>
 __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap,
     const float* __restrict__ scores, int topk, int nchunks,
@@ -44,22 +46,25 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
   int32_t* oi = final_idx ? final_idx + row * topk : out_idx + (row * nchunks + chunk) * topk;
   uint32_t* ok = final_idx ? nullptr : out_key + (row * nchunks + chunk) * topk;
   const float* s = scores + row * N_cap + j0;
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scores) + row * score_stride(N_cap, 1) + j0;
+  auto keyat = [&](int p) { return SBF ? score_key_bf16(bf16_bits_to_f32(s16[p])) : score_key(s[p]); };
+  constexpr int ksh = SBF ? 16 : 0;
 
   if (n <= topk) {  // every entry of the chunk is selected
     for (int p = tid; p < topk; p += kTkThreads) {
       const bool v = p < n;
-      const float x = s[v ? p : 0];
+      const uint32_t x = keyat(v ? p : 0);
       oi[p] = v ? j0 + p : -1;
-      if (ok) ok[p] = v ? score_key(x) : 0u;
+      if (ok) ok[p] = v ? x : 0u;
     }
     return;
   }
   uint32_t key[KPT];
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) key[u] = score_key(s[min(u * kTkThreads + tid, n - 1)]);
+  for (int u = 0; u < KPT; ++u) key[u] = keyat(min(u * kTkThreads + tid, n - 1)) >> ksh;
   block_select<kTkThreads, KPT>(key, n, topk, S, [&](int slot, int u) {
     oi[slot] = j0 + u * kTkThreads + tid;
-    if (ok) ok[slot] = key[u];
+    if (ok) ok[slot] = key[u] << ksh;
   });
 }
 
@@ -153,21 +158,37 @@ size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk) {
 }
 
 int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, const float* scores,
-                int topk, int32_t* idx_out, void* ws, hipStream_t stream) {
+                int sbf, int topk, int32_t* idx_out, void* ws, hipStream_t stream) {
   const int64_t rows = (int64_t)B * Lq;
   if (rows == 0) return 0;
   const int64_t n_max = (q_pos0 + Lq) / m;
   const int nc = max(1, topk_nchunks(n_max));
   const dim3 block(kTkThreads);
+#define CSA_TOPK_CHUNK(kpt, SB, ...)                                                           \
+  switch (kpt) {                                                                              \
+    case 4: hipLaunchKernelGGL((topk_chunk_kernel<4, SB>), __VA_ARGS__); break;               \
+    case 8: hipLaunchKernelGGL((topk_chunk_kernel<8, SB>), __VA_ARGS__); break;               \
+    case 16: hipLaunchKernelGGL((topk_chunk_kernel<16, SB>), __VA_ARGS__); break;             \
+    default: hipLaunchKernelGGL((topk_chunk_kernel<32, SB>), __VA_ARGS__); break;             \
+  }
   if (nc == 1) {
-    CSA_TOPK_KPT(kpt_for(n_max), topk_chunk_kernel, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m,
-                 N_cap, scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr);
+    if (sbf)
+      CSA_TOPK_CHUNK(kpt_for(n_max), true, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m, N_cap,
+                     scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr)
+    else
+      CSA_TOPK_CHUNK(kpt_for(n_max), false, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m, N_cap,
+                     scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr)
     return hipGetLastError() == hipSuccess ? 0 : 1;
   }
+#undef CSA_TOPK_CHUNK
   uint32_t* k0 = (uint32_t*)ws;
   int32_t* i0 = (int32_t*)(k0 + rows * nc * topk);
-  hipLaunchKernelGGL(topk_chunk_kernel<kKPT>, dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0, q_pos,
-                     m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
+  if (sbf)
+    hipLaunchKernelGGL((topk_chunk_kernel<kKPT, true>), dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0,
+                       q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
+  else
+    hipLaunchKernelGGL((topk_chunk_kernel<kKPT, false>), dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0,
+                       q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
   if (hipGetLastError() != hipSuccess) return 1;
   return launch_topk_merge(rows, nc, topk, ws, idx_out, stream);
 }

@@ -107,6 +107,29 @@ def decode(arr, fmt, scales=None):
 
 
 # ------------------------------------------------------------------ encoders
+def f64_to_bf16(x):
+    """float64 -> uint16 bf16 bit patterns, round to nearest even (finite x).
+
+    The value's binade has 8 significant bits in bf16 (7 stored), so x is
+    rounded to a multiple of 2**(e-7), e = floor(log2 |x|), with np.rint
+    (ties to even); below the smallest normal (2**-126) the step is 2**-133.
+    The rounded value is then exactly a float32 whose upper 16 bits are the
+    code.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(e2 - 1, -126)
+    step = np.ldexp(1.0, (e - 7).astype(np.int64))
+    q = np.copysign(np.rint(a / step) * step, x)
+    return (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def round_bf16(x):
+    """float64 rounded to the nearest bf16 value (ties to even), as float64."""
+    return bf16_to_f64(f64_to_bf16(x))
+
+
 _E4M3_MAX = 448.0
 
 

@@ -11,6 +11,8 @@ are not on the pages; this build fixes them:
 """
 import numpy as np
 
+from .formats import round_bf16
+
 
 def topk_select(scores, k):
     """scores: [n] finite floats of the visible entries. Returns int64 [k]."""
@@ -38,3 +40,13 @@ def topk_batch(scores, k, q_pos0, m):
             assert n <= N, "score row does not hold every visible entry"
             out[b, i] = topk_select(scores[b, i, :n], k)
     return out
+
+
+def topk_batch_bf16(scores, k, q_pos0, m):
+    """[P1] section FP4 量化: the indexer scores rounded from FP32 to BF16.
+    The top-k of the rounded scores (nearest even) under the same rule, so
+    entries whose scores round alike are ordered by index."""
+    s = np.asarray(scores, dtype=np.float64)
+    fin = np.isfinite(s)
+    r = np.where(fin, round_bf16(np.where(fin, s, 0.0)), s)
+    return topk_batch(r, k, q_pos0, m)

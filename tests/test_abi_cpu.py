@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 19, syms
+    assert len(syms) == 20, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -181,3 +181,15 @@ def test_state_and_varlen_reject(lib):
     hb = [2, 1, P, 1000, 128, 4, 128, 1, P, 6, P, P, 8, P, P, 8, None, P, None, P, nh, None]
     assert h(*hb) == SHAPE                                # n(1000) = 7 entries need N_cap >= 7
     assert h(*hb[:2], None, *hb[3:]) == NULL
+
+
+def test_index_topk_ex_rejects(lib):
+    f = lib.csa_index_topk_ex
+    n = lib.csa_index_topk_ws_bytes(1, 4, 200, 4, 64, 8)
+    base = [1, 4, None, 200, 4, 64, 4, 32, 1, P, None, P, P, None, 8, 1, P, P, n, None]
+    bad = list(base); bad[15] = 2
+    assert f(*bad) == DTYPE                       # scores in fp8: not offered
+    bad = list(base); bad[5] = 50
+    assert f(*bad) == SHAPE                       # n(203) = 51 > N_cap
+    bad = list(base); bad[18] = n - 4
+    assert f(*bad) == WS

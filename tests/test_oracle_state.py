@@ -63,6 +63,19 @@ def test_e4m3_brute_force_nearest():
             assert formats.f64_to_e4m3fn(np.array([xi]))[0] % 2 == 0
 
 
+# ------------------------------------------------------------------ bf16
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))
+    # exact midpoints between neighbouring bf16 values (ties) and zeros
+    c = rng.integers(0, 0x7F7F, 2000).astype(np.uint16)
+    lo, hi = formats.bf16_to_f64(c), formats.bf16_to_f64(c + 1)
+    x = np.concatenate([x, (lo + hi) / 2, -(lo + hi) / 2, [0.0, -0.0]])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(formats.f64_to_bf16(x), ref)
+    assert np.array_equal(formats.round_bf16(x), torch.from_numpy(x).to(torch.bfloat16).double().numpy())
+
+
 # ------------------------------------------------------------- e2m1 / MX
 def test_e2m1_encodes_ocp_table():
     rows = [l.split() for l in open(os.path.join(GOLD, "e2m1_ocp_mx.txt")) if l.strip() and not l.startswith("#")]
