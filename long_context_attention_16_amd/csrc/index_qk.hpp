@@ -363,12 +363,17 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
       return;
     }
     uint32_t key[kSelKPT];
+    {
+      float v[kSelKPT];
+      load_run<kSelKPT>(s_sc, (int)threadIdx.x * kSelKPT, n, v);
 #pragma unroll
-    for (int u = 0; u < kSelKPT; ++u) key[u] = keyof(s_sc[min(u * kSelThreads + (int)threadIdx.x, n - 1)]) >> ksh;
+      for (int u = 0; u < kSelKPT; ++u) key[u] = keyof(v[u]) >> ksh;
+    }
     block_select<kSelThreads, kSelKPT>(key, n, topk, s_sel, [&](int slot, int u) {
-      ok[slot] = key[u] << ksh;
-      oi[slot] = col0 + u * kSelThreads + (int)threadIdx.x;
+      s_sel.stage[slot] = key[u] << ksh;
+      s_sel.hist[slot] = col0 + (int)threadIdx.x * kSelKPT + u;
     });
+    block_select_out(s_sel, topk, oi, ok);
   }
 }
 

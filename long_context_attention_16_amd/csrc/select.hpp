@@ -3,12 +3,14 @@
 // kernels and the indexer's fused per-chunk selection.
 //
 // Keys live in registers, KPT per thread, key[u] of thread t at position
-// THREADS*u + t. A radix select on digits of at most 11 bits counts into an
-// LDS histogram (each thread owns kTopkBins / THREADS bins for the search);
-// every prefix sum is a DPP wave scan plus one LDS exchange of wave totals.
-// Compaction counts, per (row u, wave), the equal and the selected keys with
-// ballots and scans those counts once each, so every selected position gets
-// its output slot in ascending order with no sort.
+// KPT*t + u (each thread owns a run of consecutive positions). A radix select
+// on digits of at most 11 bits counts into an LDS histogram (each thread owns
+// kTopkBins / THREADS bins for the search); every prefix sum is a DPP wave
+// scan plus one LDS exchange of wave totals. Compaction: a thread's selected
+// keys are a bit mask over its run, so one exclusive scan of the per-thread
+// counts gives every selected position its output slot in ascending order
+// (and, when keys equal to the threshold must be ranked, one more scan of
+// the per-thread counts of equal keys), with no sort and no per-row ballots.
 #pragma once
 #include "common.hpp"
 
@@ -17,18 +19,17 @@ namespace csa {
 constexpr int kTopkBins = 2048;
 
 template <int THREADS, int KPT> struct TopkShared {
+  // the radix histogram; after the search, free for staging the selected
+  // entries' indices (with `stage` for their keys), so they reach HBM in
+  // coalesced stores (emit scatters one slot per selected key)
   int hist[kTopkBins];
+  uint32_t stage[kTopkBins];
   uint32_t wmin[THREADS / kWave], wmax[THREADS / kWave];
   int wtot[2][THREADS / kWave];
-  int cnt[KPT * (THREADS / kWave)];  // per (row, wave) counts, scanned in place
   uint32_t sel_digit;
   int sel_above;
   int sel_count;  // keys in the selected digit's bin
 };
-
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Inclusive scan over the 64 lanes of a wave with DPP moves: shifts by 1, 2,
 // 4 and 8 lanes within each row of 16, then the last lane of row 0 added to
@@ -88,7 +89,7 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], uint3
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
-    if (u * THREADS + tid < n && ((key[u] - base) & pmask) == prefix)
+    if (tid * KPT + u < n && ((key[u] - base) & pmask) == prefix)
       atomicAdd(&S.hist[((key[u] - base) >> shift) & dmask], 1);
   __syncthreads();
   const int nb = (int)dmask + 1;
@@ -120,14 +121,13 @@ __device__ __forceinline__ uint32_t radix_pass(const uint32_t (&key)[KPT], uint3
 }
 
 // Top k (k < n <= THREADS*KPT) of the register keys, key[u] of thread t being
-// position THREADS*u + t; emit(slot, u) on the threads whose key[u] is
-// selected, slots ascending with position.
+// position KPT*t + u; emit(slot, u) on the threads whose key[u] is selected,
+// slots ascending with position. emit may write S.hist and S.stage
+// (k <= kTopkBins); block_select_out copies them out after a barrier.
 template <int THREADS, int KPT, class Emit>
 __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, int k, TopkShared<THREADS, KPT>& S,
                                              const Emit& emit) {
   constexpr int NW = THREADS / kWave;
-  constexpr int NC = KPT * NW;  // (row, wave) count cells, each at most 64
-  static_assert(NC <= THREADS, "one scan pass over the count cells");
   const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   int par = 0, above, bc;
   // Keys are counted as key - min over the valid keys, and digits cover only
@@ -137,7 +137,7 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int u = 0; u < KPT; ++u)
-    if (u * THREADS + tid < n) { mn = min(mn, key[u]); mx = max(mx, key[u]); }
+    if (tid * KPT + u < n) { mn = min(mn, key[u]); mx = max(mx, key[u]); }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
@@ -188,50 +188,68 @@ __device__ __forceinline__ void block_select(const uint32_t (&key)[KPT], int n, 
   uint32_t take = 0;  // bit u: key[u] is selected
   if (all_eq) {
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) take |= (uint32_t)(u * THREADS + tid < n && key[u] >= T) << u;
+    for (int u = 0; u < KPT; ++u) take |= (uint32_t)(tid * KPT + u < n && key[u] >= T) << u;
   } else {
-    // ranks of the keys equal to T, in position order (row-major over (u, wave, lane))
+    // keys above T are taken; of the keys equal to T the need_eq first in
+    // position order, ranked by a scan of each thread's count of them
+    uint32_t eq = 0;
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const uint64_t me = __ballot(u * THREADS + tid < n && key[u] == T);
-      if (lane == 0) S.cnt[u * NW + w] = __popcll(me);
+      const bool ok = tid * KPT + u < n;
+      take |= (uint32_t)(ok && key[u] > T) << u;
+      eq |= (uint32_t)(ok && key[u] == T) << u;
     }
-    __syncthreads();
-    {
-      const int c = tid < NC ? S.cnt[tid] : 0;
-      const int off = block_scan<THREADS, KPT>(c, &tot, S, par);
-      __syncthreads();
-      if (tid < NC) S.cnt[tid] = off;
-      __syncthreads();
-    }
+    int r = block_scan<THREADS, KPT>(__popc(eq), &tot, S, par);
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-      const bool ok = u * THREADS + tid < n;
-      const bool e = ok && key[u] == T;
-      const uint64_t me = __ballot(e);
-      const bool sel = (ok && key[u] > T) || (e && S.cnt[u * NW + w] + lanes_below(me) < need_eq);
-      take |= (uint32_t)sel << u;
+      const bool e = (eq >> u) & 1u;
+      take |= (uint32_t)(e && r < need_eq) << u;
+      r += e;
     }
   }
-  __syncthreads();
+  int slot = block_scan<THREADS, KPT>(__popc(take), &tot, S, par);
 #pragma unroll
   for (int u = 0; u < KPT; ++u) {
-    const uint64_t ms = __ballot((take >> u) & 1);
-    if (lane == 0) S.cnt[u * NW + w] = __popcll(ms);
+    if ((take >> u) & 1u) emit(slot, u);
+    slot += (take >> u) & 1u;
   }
-  __syncthreads();
-  {
-    const int c = tid < NC ? S.cnt[tid] : 0;
-    const int off = block_scan<THREADS, KPT>(c, &tot, S, par);
-    __syncthreads();
-    if (tid < NC) S.cnt[tid] = off;
-    __syncthreads();
-  }
+}
+
+// v[u] = src[min(p0 + u, n - 1)], u < KPT (n >= 1): this thread's run of
+// positions. A run entirely below n is read as whole vectors of up to 16
+// bytes (the source need only be 4-byte aligned; the vector type says so).
+typedef uint32_t sel_u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t sel_u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+template <int KPT, typename E>
+__device__ __forceinline__ void load_run(const E* src, int p0, int n, E (&v)[KPT]) {
+  constexpr int BYTES = KPT * (int)sizeof(E) < 16 ? KPT * (int)sizeof(E) : 16;
+  constexpr int PER = BYTES / (int)sizeof(E);
+  static_assert(KPT % PER == 0 && (BYTES == 16 || BYTES == 8), "runs of whole 8- or 16-byte vectors");
+  if (p0 + KPT <= n) {
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const bool sel = (take >> u) & 1;
-    const uint64_t ms = __ballot(sel);
-    if (sel) emit(S.cnt[u * NW + w] + lanes_below(ms), u);
+    for (int c = 0; c < KPT / PER; ++c) {
+      if constexpr (BYTES == 16) {
+        const sel_u32x4 x = *reinterpret_cast<const sel_u32x4*>(src + p0 + c * PER);
+        __builtin_memcpy(&v[c * PER], &x, 16);
+      } else {
+        const sel_u32x2 x = *reinterpret_cast<const sel_u32x2*>(src + p0 + c * PER);
+        __builtin_memcpy(&v[c * PER], &x, 8);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) v[u] = src[min(p0 + u, n - 1)];
+  }
+}
+
+// Write the k slots staged by an emit into S.hist (indices) and S.stage
+// (keys, if okey) to HBM with consecutive threads on consecutive slots.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void block_select_out(TopkShared<THREADS, KPT>& S, int k, int32_t* oidx, uint32_t* okey) {
+  __syncthreads();
+  for (int p = threadIdx.x; p < k; p += THREADS) {
+    oidx[p] = S.hist[p];
+    if (okey) okey[p] = S.stage[p];
   }
 }
 

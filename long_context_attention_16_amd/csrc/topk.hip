@@ -29,13 +29,15 @@ constexpr int kTkKeys = kTkThreads * kKPT;     // 32768
 // nullptr: the row fits one chunk and the final indices are written;
 // otherwise the chunk's list of k (key, index), padded with key 0 / index -1.
 // SBF: bf16 scores in rows of score_stride(N_cap, 1) entries, selected on
-// 16-bit keys (score_key_bf16 >> 16).
-template <int KPT, bool SBF>
-__global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
+// 16-bit keys (score_key_bf16 >> 16). THREADS: the workgroup's width (1024
+// for few rows; narrower ones, with 32 keys per thread, put more rows in
+// flight per CU when there are many: the selection is a latency chain).
+template <int THREADS, int KPT, bool SBF>
+__global__ __launch_bounds__(THREADS) void topk_chunk_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap,
     const float* __restrict__ scores, int topk, int nchunks,
     int32_t* __restrict__ final_idx, uint32_t* __restrict__ out_key, int32_t* __restrict__ out_idx) {
-  __shared__ TopkShared<kTkThreads, KPT> S;
+  __shared__ TopkShared<THREADS, KPT> S;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / nchunks;
   const int chunk = (int)(blockIdx.x % nchunks);
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
   constexpr int ksh = SBF ? 16 : 0;
 
   if (n <= topk) {  // every entry of the chunk is selected
-    for (int p = tid; p < topk; p += kTkThreads) {
+    for (int p = tid; p < topk; p += THREADS) {
       const bool v = p < n;
       const uint32_t x = keyat(v ? p : 0);
       oi[p] = v ? j0 + p : -1;
@@ -60,12 +62,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(
     return;
   }
   uint32_t key[KPT];
+  if constexpr (SBF) {
+    uint16_t v[KPT];
+    load_run<KPT>(s16, tid * KPT, n, v);
 #pragma unroll
-  for (int u = 0; u < KPT; ++u) key[u] = keyat(min(u * kTkThreads + tid, n - 1)) >> ksh;
-  block_select<kTkThreads, KPT>(key, n, topk, S, [&](int slot, int u) {
-    oi[slot] = j0 + u * kTkThreads + tid;
-    if (ok) ok[slot] = key[u] << ksh;
+    for (int u = 0; u < KPT; ++u) key[u] = score_key_bf16(bf16_bits_to_f32(v[u])) >> 16;
+  } else {
+    float v[KPT];
+    load_run<KPT>(s, tid * KPT, n, v);
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) key[u] = score_key(v[u]);
+  }
+  block_select<THREADS, KPT>(key, n, topk, S, [&](int slot, int u) {
+    S.hist[slot] = j0 + tid * KPT + u;
+    S.stage[slot] = key[u] << ksh;
   });
+  block_select_out(S, topk, oi, ok);
 }
 
 // Merge level: workgroup = (row, group of G consecutive lists of k). The
@@ -94,16 +106,13 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(
   }
   uint32_t key[KPT];
   int32_t idx[KPT];
-#pragma unroll
-  for (int u = 0; u < KPT; ++u) {
-    const int p = min(u * kTkThreads + tid, n - 1);
-    key[u] = ik[p];
-    idx[u] = ii[p];
-  }
+  load_run<KPT>(ik, tid * KPT, n, key);
+  load_run<KPT>(ii, tid * KPT, n, idx);
   block_select<kTkThreads, KPT>(key, n, topk, S, [&](int slot, int u) {
-    oi[slot] = idx[u];
-    if (ok) ok[slot] = key[u];
+    S.hist[slot] = idx[u];
+    S.stage[slot] = key[u];
   });
+  block_select_out(S, topk, oi, ok);
 }
 
 // Keys per thread of a 1024-thread selection over up to n keys: the work of
@@ -164,31 +173,43 @@ int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int6
   const int64_t n_max = (q_pos0 + Lq) / m;
   const int nc = max(1, topk_nchunks(n_max));
   const dim3 block(kTkThreads);
-#define CSA_TOPK_CHUNK(kpt, SB, ...)                                                           \
-  switch (kpt) {                                                                              \
-    case 4: hipLaunchKernelGGL((topk_chunk_kernel<4, SB>), __VA_ARGS__); break;               \
-    case 8: hipLaunchKernelGGL((topk_chunk_kernel<8, SB>), __VA_ARGS__); break;               \
-    case 16: hipLaunchKernelGGL((topk_chunk_kernel<16, SB>), __VA_ARGS__); break;             \
-    default: hipLaunchKernelGGL((topk_chunk_kernel<32, SB>), __VA_ARGS__); break;             \
+  // Rows of one chunk: with many rows (at least four workgroups per CU) a
+  // row takes the narrowest workgroup that holds it at 32 keys per thread.
+  const bool narrow = rows >= 1024 && n_max <= 16384;
+#define CSA_TOPK_CHUNK(SB, ...)                                                                          \
+  if (narrow && n_max <= 8192) hipLaunchKernelGGL((topk_chunk_kernel<256, 32, SB>), dim3((unsigned)rows), \
+                                                  dim3(256), __VA_ARGS__);                              \
+  else if (narrow) hipLaunchKernelGGL((topk_chunk_kernel<512, 32, SB>), dim3((unsigned)rows), dim3(512),  \
+                                      __VA_ARGS__);                                                     \
+  else switch (kpt_for(n_max)) {                                                                        \
+    case 4: hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, 4, SB>), dim3((unsigned)rows), block,       \
+                               __VA_ARGS__); break;                                                     \
+    case 8: hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, 8, SB>), dim3((unsigned)rows), block,       \
+                               __VA_ARGS__); break;                                                     \
+    case 16: hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, 16, SB>), dim3((unsigned)rows), block,     \
+                                __VA_ARGS__); break;                                                    \
+    default: hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, 32, SB>), dim3((unsigned)rows), block,     \
+                                __VA_ARGS__); break;                                                    \
   }
   if (nc == 1) {
-    if (sbf)
-      CSA_TOPK_CHUNK(kpt_for(n_max), true, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m, N_cap,
-                     scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr)
-    else
-      CSA_TOPK_CHUNK(kpt_for(n_max), false, dim3((unsigned)rows), block, 0, stream, Lq, q_pos0, q_pos, m, N_cap,
-                     scores, topk, 1, idx_out, (uint32_t*)nullptr, (int32_t*)nullptr)
+    if (sbf) {
+      CSA_TOPK_CHUNK(true, 0, stream, Lq, q_pos0, q_pos, m, N_cap, scores, topk, 1, idx_out, (uint32_t*)nullptr,
+                     (int32_t*)nullptr)
+    } else {
+      CSA_TOPK_CHUNK(false, 0, stream, Lq, q_pos0, q_pos, m, N_cap, scores, topk, 1, idx_out, (uint32_t*)nullptr,
+                     (int32_t*)nullptr)
+    }
     return hipGetLastError() == hipSuccess ? 0 : 1;
   }
 #undef CSA_TOPK_CHUNK
   uint32_t* k0 = (uint32_t*)ws;
   int32_t* i0 = (int32_t*)(k0 + rows * nc * topk);
   if (sbf)
-    hipLaunchKernelGGL((topk_chunk_kernel<kKPT, true>), dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0,
-                       q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
+    hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, kKPT, true>), dim3((unsigned)(rows * nc)), block, 0, stream,
+                       Lq, q_pos0, q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
   else
-    hipLaunchKernelGGL((topk_chunk_kernel<kKPT, false>), dim3((unsigned)(rows * nc)), block, 0, stream, Lq, q_pos0,
-                       q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
+    hipLaunchKernelGGL((topk_chunk_kernel<kTkThreads, kKPT, false>), dim3((unsigned)(rows * nc)), block, 0, stream,
+                       Lq, q_pos0, q_pos, m, N_cap, scores, topk, nc, (int32_t*)nullptr, k0, i0);
   if (hipGetLastError() != hipSuccess) return 1;
   return launch_topk_merge(rows, nc, topk, ws, idx_out, stream);
 }

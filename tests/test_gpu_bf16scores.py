@@ -69,3 +69,24 @@ def test_index_topk_bf16_recall():
     rec = np.mean([len(np.intersect1d(a[r], b[r])) / s.topk for r in range(B)])
     assert np.all(np.diff(b, axis=1) > 0) and b.min() >= 0 and b.max() < n
     assert rec >= 0.99, rec
+
+
+@pytest.mark.parametrize("Lq,q_pos0,topk,prec", [
+    (1100, 9000, 100, "bf16"),     # >= 1024 rows of <= 8192 entries: 256-thread workgroups
+    (1024, 40000, 1024, "bf16"),   # <= 16384 entries: 512-thread workgroups
+    (1024, 40000, 1024, "f32"),
+    (1100, 9000, 100, "f32"),
+])
+def test_topk_many_rows_exact(Lq, q_pos0, topk, prec):
+    """Many query rows (a prefill chunk): the narrow top-k workgroups, exact on
+    integer indexer inputs, with f32 and with bf16 scores."""
+    fmt, H_i, d_i, m = "fp8", 4, 32, 4
+    N_cap = (q_pos0 + Lq) // m + 1
+    s = wl.small_shape(B=1, Lq=Lq, H_I=H_i, d_I=d_i, N_cap=N_cap, idx=fmt, exact=True)
+    x = wl.indexer_inputs(s, _gen(Lq + topk), DEV)
+    idx = csa.index_topk_ex(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, fmt, prec)
+    torch.cuda.synchronize()
+    sc = oidx.index_scores_batch(dec(x["q_i"], fmt), dec(x["w_i"], "f32"), dec(x["k_i"], fmt), q_pos0, m)
+    fin = np.where(np.isfinite(sc), sc, 0.0)
+    want = otopk.topk_batch_bf16(sc, topk, q_pos0, m) if prec == "bf16" else otopk.topk_batch(fin, topk, q_pos0, m)
+    assert np.array_equal(idx.cpu().numpy(), want)
