@@ -15,7 +15,9 @@ indexer_fp8_prefill (the fp8 indexer of a 4096-token prefill chunk at 64K
 context with 64 heads x 128 dims), compress (the compressor's bandwidth) and
 csa_decode_state (the CSA decode step with the state cache: token append and
 block compression, then indexer top-k and attention with a position per
-sequence around 128K).
+sequence around 128K) and indexer_bf16_scores (the literal fp8 4 x 32 indexer
+and top-1024 of a 4096-token prefill chunk at 64K with f32 and with bf16
+scores: speedup and recall).
 
 Prints one JSON line. The CPU baseline times the CPU oracle (test
 infrastructure) on a bounded sample of the same workload on the host cores.
@@ -41,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode",
                     choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress",
-                             "csa_decode_state"])
+                             "csa_decode_state", "indexer_bf16_scores"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB copy (calibration run for HBM byte counters)")
@@ -333,6 +335,139 @@ def bench_state_decode(args, torch, csa, wl, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_bf16_scores(args, torch, csa, wl, dev):
+    """csa_index_topk_ex on the prefill chunk (4096 queries at 61440.., 16384
+    compressed entries, literal fp8 indexer 4 x 32, top-1024, N(0,1) inputs)
+    with f32 and with bf16 scores: the scores make a round trip through HBM
+    (268 MB of f32 written and read), so their precision sets the time.
+    Recall = mean over queries of |bf16 selection & f32 selection| / k.
+    HIP-graph replays of back-to-back calls, two input sets alternating."""
+    from dataclasses import replace
+    s = replace(wl.CFG3, exact=False)
+    xs = []
+    for sd in (wl.SEEDS["3"], 1000 + wl.SEEDS["3"]):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(sd)
+        x = wl.indexer_inputs(s, gen, dev)
+        nb = csa.index_topk_ws_bytes(s.B, s.Lq, s.q_pos0, s.m, s.N_cap, s.topk)
+        x["ws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        x["out"] = {p: torch.empty((s.B, s.Lq, s.topk), dtype=torch.int32, device=dev) for p in ("f32", "bf16")}
+        xs.append(x)
+
+    for x in xs:
+        x["sc"] = {"f32": torch.empty((s.B, s.Lq, s.N_cap), dtype=torch.float32, device=dev),
+                   "bf16": torch.empty((s.B, s.Lq, (s.N_cap + 1) // 2 * 2), dtype=torch.bfloat16, device=dev)}
+
+    def call(x, prec):
+        csa.index_topk_ex(x["q_i"], x["w_i"], x["k_i"], s.topk, s.q_pos0, s.m, s.idx, prec, None, x["q_i_scale"],
+                          x["k_i_scale"], ws=x["ws"], out=x["out"][prec])
+
+    def scores_only(x, prec):
+        csa.index_scores_ex(x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, prec, None, x["q_i_scale"],
+                            x["k_i_scale"], out=x["sc"][prec])
+
+    us, us_idx = {}, {}
+    for prec in ("f32", "bf16"):
+        for k in range(4):
+            scores_only(xs[k % 2], prec)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(10):
+                scores_only(xs[k % 2], prec)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us_idx[prec] = 1000.0 * e0.elapsed_time(e1) / 50
+    for prec in ("f32", "bf16"):
+        for k in range(max(args.warmup, 2)):
+            call(xs[k % 2], prec)
+        torch.cuda.synchronize()
+        reps = 10
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for k in range(reps):
+                call(xs[k % 2], prec)
+        g.replay()
+        torch.cuda.synchronize()
+        n_rep = max(1, args.steps // reps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_rep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us[prec] = 1000.0 * e0.elapsed_time(e1) / (n_rep * reps)
+    # recall of the bf16 selection against the f32 one (last call of each on set 1)
+    a, b = xs[1]["out"]["f32"][0], xs[1]["out"]["bf16"][0]
+    mark = torch.zeros((s.Lq, s.N_cap + 1), dtype=torch.int8, device=dev)
+    mark.scatter_(1, torch.where(a >= 0, a, s.N_cap).long(), 1)
+    hit = torch.gather(mark, 1, torch.where(b >= 0, b, s.N_cap).long()).float()
+    valid = (a >= 0).float().sum(1).clamp(min=1)
+    recall = float(((hit * (b >= 0).float()).sum(1) / valid).mean())
+
+    vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
+    n_last = (s.q_pos0 + s.Lq) // s.m
+    base = s.B * n_last * s.d_I + s.B * s.Lq * s.H_I * (s.d_I + 4) + s.B * s.Lq * s.topk * 4
+    nbytes = {p: base + 2 * s.B * vis * (4 if p == "f32" else 2) for p in ("f32", "bf16")}
+    roof = {"bound": "hbm", "achieved": nbytes["bf16"] / (us["bf16"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update(traffic=None, kernel="index_topk_ex bf16 (indexer scores + chunk top-k + merge)",
+                bytes_per_launch=nbytes["bf16"])
+    roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
+    result = {
+        "metric": "indexer top-k query-tok/s with bf16 scores (prefill chunk 4096 @64K)",
+        "value": round(s.Lq / (us["bf16"] * 1e-6), 1), "unit": "query-tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us["bf16"] / 1000.0, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) indexer queries and keys in e4m3fn, random head weights)",
+        "config": {"workload": "indexer_bf16_scores_chunk4096_ctx64k_fp8", "query_chunk": s.Lq,
+                   "context": s.q_pos0 + s.Lq, "compressed_entries": s.N_cap,
+                   "indexer": "%dx%d %s" % (s.H_I, s.d_I, s.idx), "topk": s.topk},
+        "roofline": roof,
+        "us_per_call": {p: round(v, 2) for p, v in us.items()},
+        "speedup_bf16_over_f32": round(us["f32"] / us["bf16"], 3), "recall_vs_f32": round(recall, 5),
+        "indexer_scores_us": {p: round(v, 2) for p, v in us_idx.items()},
+        "indexer_speedup_bf16_over_f32": round(us_idx["f32"] / us_idx["bf16"], 3),
+        "indexer_scores_gbs": {p: round((base - s.B * s.Lq * s.topk * 4 + s.B * vis * (4 if p == "f32" else 2))
+                                        / (v * 1e-6) / 1e9, 1) for p, v in us_idx.items()},
+        "timing": "HIP-graph replays of back-to-back calls, two input sets alternating",
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _oracle_bf16_baseline(s, xs[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _oracle_bf16_baseline(s, x, seconds):
+    """The oracle's indexer scores and bf16-score top-k, query by query, until
+    `seconds` of oracle work have run."""
+    import numpy as np
+    import torch
+    from oracle import formats, indexer as oidx, topk as otopk
+    ki = x["k_i"][0].cpu().numpy()
+    done, spent = 0, 0.0
+    while done < s.Lq and (done == 0 or spent < seconds):
+        i = done
+        qi, wi = x["q_i"][0, i].cpu().numpy(), x["w_i"][0, i].cpu().numpy()
+        t0 = time.perf_counter()
+        n = (s.q_pos0 + i + 1) // s.m
+        sc = oidx.index_scores(formats.e4m3fn_to_f64(qi), wi.astype(np.float64), formats.e4m3fn_to_f64(ki[:n]))
+        r = formats.round_bf16(sc)
+        otopk.topk_select(r, s.topk)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done / spent, 3), "unit": "query-tok/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": "%d of %d queries of indexer_bf16_scores_chunk4096_ctx64k_fp8, %.1f s of oracle work "
+                      "(numpy float64)" % (done, s.Lq, spent)}
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
@@ -489,6 +624,9 @@ def main():
         return
     if W == "csa_decode_state":
         bench_state_decode(args, torch, csa, wl, dev)
+        return
+    if W == "indexer_bf16_scores":
+        bench_bf16_scores(args, torch, csa, wl, dev)
         return
     if W == "csa_decode":
         shapes = [("", wl.CFG2)]

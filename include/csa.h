@@ -342,6 +342,20 @@ int csa_index_topk_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int m
                       const void* k_i, const uint8_t* k_i_scale,
                       int topk, int score_dtype, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * csa_index_scores_ex — the indexer step of csa_index_topk_ex alone: the
+ * scores of csa_index_scores, with optional per-sequence positions (q_pos as
+ * in csa_index_topk_ex) and stored as float32 (score_dtype = CSA_F32, rows of
+ * N_cap entries) or as bfloat16 bits rounded to nearest even (CSA_BF16, rows
+ * of N_cap rounded up to even entries: scores [B, Lq, (N_cap+1)/2*2]
+ * uint16). Entries j >= n(t) of a row are unspecified for bf16 (a bf16 word
+ * pairs entries j and j+1) and untouched for f32. No workspace.
+ */
+int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int m, int64_t N_cap,
+                        int H_i, int d_i, int idx_dtype,
+                        const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                        const void* k_i, const uint8_t* k_i_scale, int score_dtype, void* scores, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,7 @@ SIGNATURES = {
                                    _P, _P, _P, _P, _Z, _P]),
     "csa_index_topk_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
                                _Z, _P]),
+    "csa_index_scores_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P]),
 }
 
 _lib = None
@@ -328,4 +329,22 @@ def index_topk_ex(q_i, w_i, k_i, topk, q_pos0, m, fmt, score_dtype="bf16", q_pos
                                    d_i, IDX_FORMATS[fmt], _ptr(q_i), _ptr(q_scale), _ptr(w_i), _ptr(k_i),
                                    _ptr(k_scale), topk, IDX_FORMATS[score_dtype], _ptr(out), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream()))
+    return out
+
+
+def index_scores_ex(q_i, w_i, k_i, q_pos0, m, fmt, score_dtype="bf16", q_pos=None, q_scale=None, k_scale=None,
+                    out=None):
+    """Indexer scores as f32 [B, Lq, N_cap] or bf16 [B, Lq, N_cap rounded up
+    to even] (nearest even); optional per-sequence positions q_pos."""
+    B, Lq, H_i = w_i.shape
+    N_cap = k_i.shape[1]
+    d_i = q_i.shape[-1] * (2 if fmt == "fp4" else 1)
+    if out is None:
+        if score_dtype == "bf16":
+            out = torch.zeros((B, Lq, (N_cap + 1) // 2 * 2), dtype=torch.bfloat16, device=q_i.device)
+        else:
+            out = torch.full((B, Lq, N_cap), float("-inf"), dtype=torch.float32, device=q_i.device)
+    _check(lib().csa_index_scores_ex(B, Lq, None if q_pos is None else _pos_tensor(q_pos), q_pos0, m, N_cap, H_i,
+                                     d_i, IDX_FORMATS[fmt], _ptr(q_i), _ptr(q_scale), _ptr(w_i), _ptr(k_i),
+                                     _ptr(k_scale), IDX_FORMATS[score_dtype], _ptr(out), _stream()))
     return out

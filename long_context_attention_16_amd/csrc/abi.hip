@@ -164,6 +164,20 @@ int csa_index_scores(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int H_
                          k_i_scale, scores, 0, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
+int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int m, int64_t N_cap, int H_i,
+                        int d_i, int idx_dtype, const void* q_i, const uint8_t* q_i_scale, const float* w_i,
+                        const void* k_i, const uint8_t* k_i_scale, int score_dtype, void* scores, void* stream) {
+  if (!scores) return CSA_ERR_NULL;
+  if (score_dtype != CSA_F32 && score_dtype != CSA_BF16) return CSA_ERR_DTYPE;
+  if (int rc = check_indexer(B, Lq, q_pos0, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                             k_i_scale, 1))
+    return rc;
+  if (!aligned16(scores)) return CSA_ERR_ALIGN;
+  return launch_index_qk(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
+                         k_i_scale, (float*)scores, score_dtype == CSA_BF16, as_stream(stream))
+             ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
 // csa_index_topk, csa_index_topk_varlen and csa_index_topk_ex: q_pos ==
 // nullptr means every sequence's row 0 is at q_pos0; otherwise q_pos0 bounds
 // the q_pos values. sbf: scores rounded to bf16 before the top-k.

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 20, syms
+    assert len(syms) == 21, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -193,3 +193,11 @@ def test_index_topk_ex_rejects(lib):
     assert f(*bad) == SHAPE                       # n(203) = 51 > N_cap
     bad = list(base); bad[18] = n - 4
     assert f(*bad) == WS
+
+    g = lib.csa_index_scores_ex
+    sb = [1, 4, None, 200, 4, 64, 4, 32, 1, P, None, P, P, None, 1, P, None]
+    assert g(*sb[:15], None, None) == NULL
+    bad = list(sb); bad[14] = 3
+    assert g(*bad) == DTYPE
+    bad = list(sb); bad[15] = MIS
+    assert g(*bad) == ALIGN

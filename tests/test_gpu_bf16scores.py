@@ -90,3 +90,30 @@ def test_topk_many_rows_exact(Lq, q_pos0, topk, prec):
     fin = np.where(np.isfinite(sc), sc, 0.0)
     want = otopk.topk_batch_bf16(sc, topk, q_pos0, m) if prec == "bf16" else otopk.topk_batch(fin, topk, q_pos0, m)
     assert np.array_equal(idx.cpu().numpy(), want)
+
+
+
+@pytest.mark.parametrize("fmt,H_i,d_i,Lq,q_pos0,extra", [
+    ("fp8", 4, 32, 9, 3000, 0),     # grouped queries, odd N_cap
+    ("bf16", 64, 128, 2, 5000, 1),
+    ("fp8", 64, 128, 20, 4001, 0),  # many-query fp8 kernel
+    ("fp4", 16, 128, 3, 2000, 2),
+])
+def test_index_scores_bf16_exact(fmt, H_i, d_i, Lq, q_pos0, extra):
+    """bf16 scores equal the oracle's scores rounded to bf16 (integer inputs:
+    the f32 scores are exact), for every visible entry; compared as values,
+    since an all-zero head sum may carry either sign of zero (-0 and +0 are
+    one score to the top-k)."""
+    m, B = 4, 2
+    N_cap = (q_pos0 + Lq) // m + extra
+    s = wl.small_shape(B=B, Lq=Lq, H_I=H_i, d_I=d_i, N_cap=N_cap, idx=fmt, exact=True)
+    x = wl.indexer_inputs(s, _gen(H_i + d_i + Lq), DEV)
+    out = csa.index_scores_ex(x["q_i"], x["w_i"], x["k_i"], q_pos0, m, fmt, "bf16", None, x["q_i_scale"],
+                              x["k_i_scale"])
+    torch.cuda.synchronize()
+    assert out.shape[-1] == (N_cap + 1) // 2 * 2
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    sc = oidx.index_scores_batch(dec(x["q_i"], fmt, x["q_i_scale"]), dec(x["w_i"], "f32"),
+                                 dec(x["k_i"], fmt, x["k_i_scale"]), q_pos0, m)
+    vis = np.isfinite(sc)
+    assert np.array_equal(formats.bf16_to_f64(got[:, :, :N_cap][vis]), formats.round_bf16(sc[vis]))
