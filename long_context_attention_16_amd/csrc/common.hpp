@@ -134,9 +134,9 @@ __host__ __device__ inline int64_t score_stride(int64_t N_cap, int sbf) { return
 // lanes swap values with one DPP move (quad_perm [1,0,3,2]); every lane
 // executes it.
 __device__ __forceinline__ uint32_t score_word(float v, int sbf) {
+  if (!sbf) return __builtin_bit_cast(uint32_t, v);
   const int nb = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false);
-  return sbf ? ((uint32_t)f32_to_bf16_bits(v) | ((uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, nb)) << 16))
-             : __builtin_bit_cast(uint32_t, v);
+  return (uint32_t)f32_to_bf16_bits(v) | ((uint32_t)f32_to_bf16_bits(__builtin_bit_cast(float, nb)) << 16);
 }
 
 }  // namespace csa

@@ -72,10 +72,14 @@ __device__ __forceinline__ constexpr int pf_vmcnt(int n) {
   return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
 }
 
+// SBF: bf16 scores (a template parameter: the f32 epilogue stays as short as
+// before, the kernel being bound by its step latency).
+template <bool SBF>
 __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const float* __restrict__ w_i, const uint8_t* __restrict__ k_i,
-    float* __restrict__ scores, int sbf) {
+    float* __restrict__ scores) {
+  constexpr int sbf = SBF ? 1 : 0;
   // Three separate arrays rather than one indexed by block: the compiler
   // then knows which ring buffer an LDS read touches and waits only for the
   // copies into that buffer, not for the blocks still in flight.
@@ -277,8 +281,12 @@ int launch_index_qk_prefill(int B, int Lq, int64_t q_pos0, const int64_t* q_pos,
   const int ngroups = (Lq + kPfQ - 1) / kPfQ;
   if (nchunks == 0 || B == 0 || Lq == 0) return 0;
   const dim3 grid((unsigned)((int64_t)B * ngroups * nchunks));
-  hipLaunchKernelGGL(index_qk_prefill_kernel, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, q_pos, m, N_cap,
-                     ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores, sbf);
+  if (sbf)
+    hipLaunchKernelGGL(index_qk_prefill_kernel<true>, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, q_pos, m,
+                       N_cap, ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores);
+  else
+    hipLaunchKernelGGL(index_qk_prefill_kernel<false>, grid, dim3(kPfWaves * kWave), 0, stream, Lq, q_pos0, q_pos, m,
+                       N_cap, ngroups, nchunks, (const uint8_t*)q_i, w_i, (const uint8_t*)k_i, scores);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
