@@ -614,13 +614,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
 // least S/16 rows), so its loads of the split partials are independent and
 // issued together rather than one dependent round trip per split.
 constexpr int kMaxSplits = 16;
-constexpr int kCombThreads = 256;
+constexpr int kCombThreads = 64;  // small workgroups: at decode sizes they still cover every CU
 template <typename T, int D, bool HCA>
 __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs p) {
   constexpr int VPT = 16 / (int)sizeof(T);  // values per thread
-  constexpr int TPH = D / VPT;              // threads per (query, head)
-  constexpr int HPB = kCombThreads / TPH;   // (query, head) rows per block
-  const int64_t row = (int64_t)blockIdx.x * HPB + threadIdx.x / TPH;
+  constexpr int TPH = D / VPT;              // threads per (query, head) row (32 to 128)
+  const int64_t gt = (int64_t)blockIdx.x * kCombThreads + threadIdx.x;
+  const int64_t row = gt / TPH;
   if (row >= (int64_t)p.B * p.Lq * p.H) return;
   const int64_t qrow = row / p.H;
   const int h = (int)(row % p.H);
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs p) 
   for (int s = 0; s < kMaxSplits; ++s)
     ml[s] = s < nsplit ? *reinterpret_cast<const float2*>(p.ws_ml + (slot0 + (int64_t)s * p.H) * 2)
                        : make_float2(-INFINITY, 0.f);
-  const int d = (threadIdx.x % TPH) * VPT;
+  const int d = (int)(gt % TPH) * VPT;
   uint4 raw[kMaxSplits];
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s)
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kCombThreads) void attn_combine_kernel(AttnArgs p) 
     for (int v = 0; v < VPT; ++v) o[v] = fmaf(w, x[v], o[v]);
   }
   *reinterpret_cast<uint4*>((T*)p.out + (qrow * p.H + h) * D + d) = Chunk<T>::pack(o);
-  if (p.lse && threadIdx.x % TPH == 0)
+  if (p.lse && gt % TPH == 0)
     p.lse[qrow * p.H + h] = M == -INFINITY ? -INFINITY : (M + log2f(den)) * kLn2;
 }
 

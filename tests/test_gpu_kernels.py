@@ -225,6 +225,7 @@ def _oracle_attn(x, fmt, idx, q_pos0, raw_pos0, W, sink, hca_m=None):
     ("bf16", 1, 3, 16, 512, 40, 0, False),    # no window, no sink
     ("f32", 1, 3, 32, 512, 24, 7, True),
     ("bf16", 1, 2, 128, 128, 300, 33, True),
+    ("f32", 1, 2, 8, 512, 300, 64, True),     # f32 rows of 512 split 4 ways: 128 combine threads per row
 ])
 def test_sparse_attn(fmt, B, Lq, H, D, k, W, sink):
     m, q_pos0 = 4, 3000
@@ -310,6 +311,7 @@ def test_sparse_attn_edges():
     ("bf16", 2, 1, 64, 512, 128, 70000, 128),   # 547 entries + window: several splits
     ("f32", 1, 6, 4, 128, 4, 250, 16),           # prefill rows with ragged n(t)
     ("bf16", 2, 3, 64, 512, 128, 126, 20),       # n(t) = 0 or 1
+    ("f32", 1, 2, 16, 512, 4, 3000, 32),         # f32 rows of 512, several splits
 ])
 def test_hca_attn(fmt, B, Lq, H, D, m, q_pos0, W):
     N_cap = (q_pos0 + Lq) // m + 1
