@@ -17,6 +17,8 @@ Sources (cited by page title and section; see each module):
        Context Intelligence" (aiorang.com), section 01 架构与基础设施优化.
   [P5] "DeepSeek V4 重磅开源！百万上下文+双算力兼容，国产大模型正式迈入新时代"
        (gitcode.csdn.net), sections 3 混合注意力机制 and 4 FP4 量化训练.
+  [P1] also, section 確定性內核: a deterministic attention backward (no
+       split-KV, fixed accumulation order) for training;
   [P1] also, section 框架層優化: the state cache (window tokens plus tokens of
        the incomplete block) kept apart from the compressed KV cache.
 
@@ -27,4 +29,4 @@ Parity status: every function here is pinned by tests in
 tests/test_oracle_*.py against closed forms, brute force, library routines or
 format tables; none is "parity unpinned" with respect to these readings.
 """
-from . import formats, rope, compress, indexer, topk, attention, state  # noqa: F401
+from . import formats, rope, compress, indexer, topk, attention, attention_bwd, state  # noqa: F401
