@@ -356,6 +356,54 @@ int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int
                         const void* q_i, const uint8_t* q_i_scale, const float* w_i,
                         const void* k_i, const uint8_t* k_i_scale, int score_dtype, void* scores, void* stream);
 
+/*
+ * csa_sparse_attn_bwd, hca_dense_attn_bwd — gradients of csa_sparse_attn /
+ * hca_dense_attn for training.
+ * [P1] 確定性內核: the attention backward is deterministic (no split-KV; a
+ * fixed result whatever the order of work) and batch-invariant. With P_hr =
+ * exp(l_hr - lse_h) the forward's weights (l_hr the scaled logit of head h
+ * and source row r, lse from the forward), dO = dout:
+ *   dP_hr = <dO_h, v_r>, Dl_h = <dO_h, o_h> (o = the forward's out),
+ *   dS_hr = P_hr (dP_hr - Dl_h);
+ *   dq_h = RoPE^T(sum_r dS_hr k_r, t) / sqrt(D)   (k_r as attended: compressed
+ *          keys as stored, window keys rotated at their position s);
+ *   dk_r = sum_h dS_hr RoPE(q_h, t) / sqrt(D), rotated back (RoPE^T at s) for
+ *          window rows; dv_r = sum_h P_hr dO_h;
+ *   dsink_h = -sum over queries of exp(z_h - lse_h) Dl_h.
+ * A row used by several queries (an entry selected by many queries of a
+ * sequence, a raw row in many windows) receives the sum of their
+ * contributions, accumulated as 64-bit integers in units of 2^-32 (exact,
+ * so the result does not depend on the order; contributions are clamped to
+ * |x| <= 2^30) and rounded once to float32.
+ *
+ * Arguments of the forward call (uniform positions, linear raw rows), plus:
+ *   out, lse    the forward's outputs ([B, Lq, H, D] in kv_dtype, [B, Lq, H] f32)
+ *   dout        [B, Lq, H, D] in kv_dtype
+ *   dq          [B, Lq, H, D] float32
+ *   dk_c, dv_c  [B, N_cap, D] float32, every row written (0 where unused)
+ *   dk_raw, dv_raw  [B, T_raw, D] float32, every row written (may be NULL
+ *               when T_raw = 0)
+ *   dsink       [H] float32 (required with a sink, else may be NULL)
+ *   ws, ws_bytes  csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)
+ *               bytes: 16 bytes per element of k_c, v_c, k_raw and v_raw plus
+ *               the per-query sink parts; no initial contents needed.
+ * hca_dense_attn_bwd: the same for hca_dense_attn (block m, every visible entry).
+ */
+size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int T_raw);
+int csa_sparse_attn_bwd(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype,
+                        const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                        int topk, const int32_t* idx,
+                        int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                        const float* sink, const void* out, const float* lse, const void* dout,
+                        float* dq, float* dk_c, float* dv_c, float* dk_raw, float* dv_raw, float* dsink,
+                        void* ws, size_t ws_bytes, void* stream);
+int hca_dense_attn_bwd(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype,
+                       const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                       int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                       const float* sink, const void* out, const float* lse, const void* dout,
+                       float* dq, float* dk_c, float* dv_c, float* dk_raw, float* dv_raw, float* dsink,
+                       void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,11 @@ SIGNATURES = {
     "csa_index_topk_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
                                _Z, _P]),
     "csa_index_scores_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P]),
+    "csa_sparse_attn_bwd_ws_bytes": (_Z, [_I, _I, _I, _I, _L, _I]),
+    "csa_sparse_attn_bwd": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "hca_dense_attn_bwd": (_I, [_I, _I, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _L, _P, _P, _I, _P, _P, _P, _P,
+                                _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
 }
 
 _lib = None
@@ -348,3 +353,42 @@ def index_scores_ex(q_i, w_i, k_i, q_pos0, m, fmt, score_dtype="bf16", q_pos=Non
                                      d_i, IDX_FORMATS[fmt], _ptr(q_i), _ptr(q_scale), _ptr(w_i), _ptr(k_i),
                                      _ptr(k_scale), IDX_FORMATS[score_dtype], _ptr(out), _stream()))
     return out
+
+
+# ------------------------------------------------------------------ backward
+def attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw):
+    return lib().csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)
+
+
+def _bwd_outputs(q, k_c, k_raw, sink):
+    B, Lq, H, D = q.shape
+    f = dict(dtype=torch.float32, device=q.device)
+    return (torch.empty((B, Lq, H, D), **f), torch.empty(k_c.shape, **f), torch.empty(k_c.shape, **f),
+            torch.empty(k_raw.shape, **f), torch.empty(k_raw.shape, **f),
+            None if sink is None else torch.empty((H,), **f))
+
+
+def sparse_attn_bwd(q, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink, q_pos0, out, lse, dout, ws=None):
+    """Gradients of sparse_attn: (dq, dk_c, dv_c, dk_raw, dv_raw, dsink), f32."""
+    B, Lq, H, D = q.shape
+    if ws is None:
+        ws = _ws(attn_bwd_ws_bytes(B, Lq, H, D, k_c.shape[1], k_raw.shape[1]), q.device)
+    g = _bwd_outputs(q, k_c, k_raw, sink)
+    _check(lib().csa_sparse_attn_bwd(B, Lq, q_pos0, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c), _ptr(v_c),
+                                     idx.shape[-1], _ptr(idx), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W,
+                                     _ptr(sink), _ptr(out), _ptr(lse), _ptr(dout), *[_ptr(x) for x in g], _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()))
+    return g
+
+
+def hca_attn_bwd(q, k_c, v_c, m, k_raw, v_raw, raw_pos0, W, sink, q_pos0, out, lse, dout, ws=None):
+    """Gradients of hca_attn: (dq, dk_c, dv_c, dk_raw, dv_raw, dsink), f32."""
+    B, Lq, H, D = q.shape
+    if ws is None:
+        ws = _ws(attn_bwd_ws_bytes(B, Lq, H, D, k_c.shape[1], k_raw.shape[1]), q.device)
+    g = _bwd_outputs(q, k_c, k_raw, sink)
+    _check(lib().hca_dense_attn_bwd(B, Lq, q_pos0, m, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c),
+                                    _ptr(v_c), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W, _ptr(sink),
+                                    _ptr(out), _ptr(lse), _ptr(dout), *[_ptr(x) for x in g], _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream()))
+    return g

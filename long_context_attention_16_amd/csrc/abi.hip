@@ -396,4 +396,55 @@ int hca_dense_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max
                     out, lse, ws, ws_bytes, stream);
 }
 
+size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int T_raw) {
+  if (B <= 0 || Lq <= 0 || H <= 0 || D <= 0 || N_cap < 0 || T_raw < 0) return 16;
+  return attn_bwd_ws_bytes(B, Lq, H, N_cap, T_raw, D);
+}
+
+// csa_sparse_attn_bwd and hca_dense_attn_bwd (m > 0: HCA, every visible entry).
+static int attn_bwd(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype, const void* q, int64_t N_cap,
+                    const void* k_c, const void* v_c, int topk, const int32_t* idx, int T_raw, int64_t raw_pos0,
+                    const void* k_raw, const void* v_raw, int W, const float* sink, const void* out,
+                    const float* lse, const void* dout, float* dq, float* dk_c, float* dv_c, float* dk_raw,
+                    float* dv_raw, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  const bool hca = m > 0;
+  if (int rc = check_attn_common(B, Lq, q_pos0, H, D, kv_dtype, q, k_c, v_c, T_raw, raw_pos0, k_raw, v_raw, W, sink,
+                                 (void*)out, (float*)lse, ws, N_cap, false))
+    return rc;
+  if (!lse || !dout || !dq || !dk_c || !dv_c || (T_raw > 0 && (!dk_raw || !dv_raw))) return CSA_ERR_NULL;
+  if (sink && !dsink) return CSA_ERR_NULL;
+  if (!hca && (topk < 0 || topk > 2048 || (topk > 0 && !idx))) return CSA_ERR_SHAPE;
+  if (hca && (m > 4096 || n_last(q_pos0, Lq, m) > N_cap)) return CSA_ERR_SHAPE;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk_c) || !aligned16(dv_c) ||
+      (T_raw > 0 && (!aligned16(dk_raw) || !aligned16(dv_raw))))
+    return CSA_ERR_ALIGN;
+  if (!ws || ws_bytes < csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)) return CSA_ERR_WORKSPACE;
+  AttnArgs a{};
+  a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = hca ? m : 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
+  a.k_c = k_c; a.v_c = v_c; a.topk = hca ? 0 : topk; a.idx = hca ? nullptr : idx; a.T_raw = T_raw;
+  a.raw_pos0 = raw_pos0; a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = (void*)out;
+  a.lse = (float*)lse;
+  return launch_attn_bwd(a, hca, kv_dtype, dout, dq, dk_c, dv_c, dk_raw, dv_raw, dsink, ws, as_stream(stream))
+             ? CSA_ERR_LAUNCH : CSA_OK;
+}
+
+int csa_sparse_attn_bwd(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q, int64_t N_cap,
+                        const void* k_c, const void* v_c, int topk, const int32_t* idx, int T_raw, int64_t raw_pos0,
+                        const void* k_raw, const void* v_raw, int W, const float* sink, const void* out,
+                        const float* lse, const void* dout, float* dq, float* dk_c, float* dv_c, float* dk_raw,
+                        float* dv_raw, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  return attn_bwd(B, Lq, q_pos0, 0, H, D, kv_dtype, q, N_cap, k_c, v_c, topk, idx, T_raw, raw_pos0, k_raw, v_raw, W,
+                  sink, out, lse, dout, dq, dk_c, dv_c, dk_raw, dv_raw, dsink, ws, ws_bytes, stream);
+}
+
+int hca_dense_attn_bwd(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_dtype, const void* q,
+                       int64_t N_cap, const void* k_c, const void* v_c, int T_raw, int64_t raw_pos0,
+                       const void* k_raw, const void* v_raw, int W, const float* sink, const void* out,
+                       const float* lse, const void* dout, float* dq, float* dk_c, float* dv_c, float* dk_raw,
+                       float* dv_raw, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1) return CSA_ERR_SHAPE;
+  return attn_bwd(B, Lq, q_pos0, m, H, D, kv_dtype, q, N_cap, k_c, v_c, 0, nullptr, T_raw, raw_pos0, k_raw, v_raw, W,
+                  sink, out, lse, dout, dq, dk_c, dv_c, dk_raw, dv_raw, dsink, ws, ws_bytes, stream);
+}
+
 }  // extern "C"

@@ -29,7 +29,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     syms = header_symbols()
-    assert len(syms) == 21, syms
+    assert len(syms) == 24, syms
     for s in syms:
         assert hasattr(lib, s), s
         assert s in csa.SIGNATURES, s
@@ -201,3 +201,23 @@ def test_index_topk_ex_rejects(lib):
     assert g(*bad) == DTYPE
     bad = list(sb); bad[15] = MIS
     assert g(*bad) == ALIGN
+
+
+
+def test_attn_bwd_rejects(lib):
+    f = lib.csa_sparse_attn_bwd
+    n = lib.csa_sparse_attn_bwd_ws_bytes(1, 1, 4, 128, 64, 8)
+    base = [1, 1, 100, 4, 128, 1, P, 64, P, P, 16, P, 8, 93, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n, None]
+    bad = list(base); bad[13] = 94
+    assert f(*bad) == SHAPE                       # window row 93 not covered
+    bad = list(base); bad[19] = None
+    assert f(*bad) == NULL                        # lse
+    bad = list(base); bad[26] = None
+    assert f(*bad) == NULL                        # dsink with a sink
+    bad = list(base); bad[28] = n - 8
+    assert f(*bad) == WS
+    bad = list(base); bad[21] = MIS
+    assert f(*bad) == ALIGN                       # dq
+    h = lib.hca_dense_attn_bwd
+    hb = [1, 1, 1000, 128, 4, 128, 1, P, 6, P, P, 8, 993, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n, None]
+    assert h(*hb) == SHAPE                        # n(1000) = 7 entries need N_cap >= 7

@@ -1,0 +1,127 @@
+"""GPU parity of the attention backward (csa_sparse_attn_bwd,
+hca_dense_attn_bwd) against the fp64 oracle's gradients, through the C ABI:
+the GPU forward's out and lse feed the GPU backward, the oracle recomputes
+everything from the same decoded inputs. Also: bitwise determinism across
+calls and batch invariance (a sequence alone and inside a batch)."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_16_amd as csa
+from oracle import attention_bwd as obwd
+from helpers import dec
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed):
+    g = _gen(seed)
+    dt = torch.float32 if fmt == "f32" else torch.bfloat16
+    r = lambda *s: torch.randn(s, generator=g, device=DEV).to(dt)
+    return dict(q=r(B, Lq, H, D), k_c=r(B, N_cap, D), v_c=r(B, N_cap, D), k_raw=r(B, T_raw, D),
+                v_raw=r(B, T_raw, D), sink=torch.randn((H,), generator=g, device=DEV), dout=r(B, Lq, H, D))
+
+
+def _idx(B, Lq, k, q_pos0, m, N_cap, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, Lq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(Lq):
+            n = min(N_cap, (q_pos0 + i + 1) // m)
+            take = min(n, int(rng.integers(max(1, k // 2), k + 1)))
+            idx[b, i, :take] = np.sort(rng.choice(n, size=take, replace=False))
+    return idx
+
+
+def _close(got, want, rel, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    scale = max(1e-6, float(np.abs(want).max()))
+    err = float(np.abs(got - want).max())
+    assert err <= rel * scale, "%s: max-abs %.3g > %.3g x max|ref| %.3g" % (what, err, rel, scale)
+
+
+def _check(fmt, g, want):
+    rel = 2e-2 if fmt == "bf16" else 2e-4
+    for name, a, b in zip(["dq", "dk_c", "dv_c", "dk_raw", "dv_raw", "dsink"], g, want):
+        if a is None:
+            continue
+        _close(a.cpu().numpy(), b, rel, name)
+
+
+@pytest.mark.parametrize("fmt,B,Lq,H,D,k,W,q_pos0,sink", [
+    ("f32", 1, 9, 4, 128, 64, 16, 300, True),     # prefill rows sharing entries and window rows
+    ("f32", 2, 3, 8, 512, 40, 7, 100, False),     # no sink
+    ("bf16", 2, 1, 64, 512, 512, 128, 5000, True),  # decode head layout
+    ("bf16", 1, 5, 16, 128, 24, 20, 10, True),    # windows cut at position 0, few entries
+    ("f32", 1, 4, 4, 128, 16, 0, 200, True),      # no window
+])
+def test_sparse_attn_bwd(fmt, B, Lq, H, D, k, W, q_pos0, sink):
+    m = 4
+    N_cap = (q_pos0 + Lq) // m + 3
+    raw_pos0 = max(0, q_pos0 - W - 2)
+    T_raw = q_pos0 + Lq - raw_pos0 + 1
+    x = _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=H + D + k)
+    idx = _idx(B, Lq, k, q_pos0, m, N_cap, seed=k + Lq)
+    it = torch.from_numpy(idx).to(DEV)
+    s = x["sink"] if sink else None
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, s, q_pos0)
+    g = csa.sparse_attn_bwd(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, s, q_pos0, out, lse,
+                            x["dout"])
+    torch.cuda.synchronize()
+    want = obwd.csa_sparse_attn_bwd(dec(x["q"], fmt), q_pos0, dec(x["k_c"], fmt), dec(x["v_c"], fmt), idx,
+                                    dec(x["k_raw"], fmt), dec(x["v_raw"], fmt), raw_pos0, W,
+                                    None if s is None else dec(s, "f32"), dec(x["dout"], fmt))
+    _check(fmt, g, want)
+
+
+@pytest.mark.parametrize("fmt,B,Lq,H,D,m,q_pos0,W", [
+    ("bf16", 1, 1, 16, 512, 128, 70000, 128),
+    ("f32", 1, 6, 4, 128, 4, 250, 16),            # prefill rows with ragged n(t)
+])
+def test_hca_attn_bwd(fmt, B, Lq, H, D, m, q_pos0, W):
+    N_cap = (q_pos0 + Lq) // m + 1
+    raw_pos0 = max(0, q_pos0 - W + 1)
+    T_raw = q_pos0 + Lq - raw_pos0
+    x = _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=D + m)
+    out, lse = csa.hca_attn(x["q"], x["k_c"], x["v_c"], m, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0)
+    g = csa.hca_attn_bwd(x["q"], x["k_c"], x["v_c"], m, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0, out,
+                         lse, x["dout"])
+    torch.cuda.synchronize()
+    want = obwd.hca_dense_attn_bwd(dec(x["q"], fmt), q_pos0, m, dec(x["k_c"], fmt), dec(x["v_c"], fmt),
+                                   dec(x["k_raw"], fmt), dec(x["v_raw"], fmt), raw_pos0, W, dec(x["sink"], "f32"),
+                                   dec(x["dout"], fmt))
+    _check(fmt, g, want)
+
+
+def test_bwd_deterministic_and_batch_invariant():
+    """Two calls give the same bits; sequence 0 alone gives the same bits as
+    inside the batch (its rows get contributions from its own queries only,
+    added exactly)."""
+    fmt, B, Lq, H, D, k, W, q_pos0, m = "bf16", 3, 6, 8, 128, 48, 16, 400, 4
+    N_cap = (q_pos0 + Lq) // m + 1
+    raw_pos0 = q_pos0 - W
+    T_raw = q_pos0 + Lq - raw_pos0
+    x = _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=9)
+    it = torch.from_numpy(_idx(B, Lq, k, q_pos0, m, N_cap, seed=3)).to(DEV)
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0)
+    args = (x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0, out, lse, x["dout"])
+    g1 = csa.sparse_attn_bwd(*args)
+    g2 = csa.sparse_attn_bwd(*args)
+    one = lambda t: t[:1].contiguous()
+    o1, l1 = csa.sparse_attn(one(x["q"]), one(x["k_c"]), one(x["v_c"]), one(it), one(x["k_raw"]), one(x["v_raw"]),
+                             raw_pos0, W, x["sink"], q_pos0)
+    g3 = csa.sparse_attn_bwd(one(x["q"]), one(x["k_c"]), one(x["v_c"]), one(it), one(x["k_raw"]), one(x["v_raw"]),
+                             raw_pos0, W, x["sink"], q_pos0, o1, l1, one(x["dout"]))
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for a, b in zip(g1[:5], g3[:5]):
+        assert torch.equal(a[:1], b)
