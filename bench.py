@@ -17,7 +17,8 @@ csa_decode_state (the CSA decode step with the state cache: token append and
 block compression, then indexer top-k and attention with a position per
 sequence around 128K) and indexer_bf16_scores (the literal fp8 4 x 32 indexer
 and top-1024 of a 4096-token prefill chunk at 64K with f32 and with bf16
-scores: speedup and recall).
+scores: speedup and recall) and csa_attn_bwd (the attention backward on the
+2048-token prefill and on the 4096-token chunk at 64K).
 
 Prints one JSON line. The CPU baseline times the CPU oracle (test
 infrastructure) on a bounded sample of the same workload on the host cores.
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode",
                     choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress",
-                             "csa_decode_state", "indexer_bf16_scores"])
+                             "csa_decode_state", "indexer_bf16_scores", "csa_attn_bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB copy (calibration run for HBM byte counters)")
@@ -468,6 +469,113 @@ def _oracle_bf16_baseline(s, x, seconds):
                       "(numpy float64)" % (done, s.Lq, spent)}
 
 
+def bench_attn_bwd(args, torch, csa, wl, dev):
+    """csa_sparse_attn_bwd on prefill attention shapes: the 2048-token prefill
+    (f32, 4 heads x 128, top-64, window 128) and the 4096-token chunk at 64K
+    (bf16, top-1024 of 16384 entries, window 128). Selected entries are random
+    sorted sets (the gather pattern N(0,1) scores give). Timed with HIP events
+    over back-to-back calls (each call: zero the accumulators, the backward
+    kernel, the f32 conversion, the sink sum). Algorithmic bytes per call:
+    per query the k + W source rows of K and V, q, dout, out and lse read once;
+    dq, and dk/dv of every compressed and raw row written once."""
+    import numpy as np
+    cases = [("prefill_L2048_f32", wl.CFG1), ("chunk4096_ctx64k_bf16", wl.CFG3)]
+    res = {}
+    for name, s in cases:
+        x = wl.make_inputs(s, wl.SEEDS["1" if s is wl.CFG1 else "3"], device=dev)
+        rng = np.random.default_rng(7)
+        idx = np.full((s.B, s.Lq, s.topk), -1, dtype=np.int32)
+        for i in range(s.Lq):
+            n = min(s.N_cap, (s.q_pos0 + i + 1) // s.m)
+            take = min(n, s.topk)
+            idx[0, i, :take] = np.sort(rng.choice(n, size=take, replace=False))
+        it = torch.from_numpy(idx).to(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        dout = torch.randn(x["q"].shape, generator=gen, device=dev).to(x["q"].dtype)
+        out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"],
+                                   s.q_pos0)
+        wsb = csa.attn_bwd_ws_bytes(s.B, s.Lq, s.H, s.D, s.N_cap, s.T_raw)
+        ws = torch.empty((wsb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+
+        def call():
+            return csa.sparse_attn_bwd(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], s.raw_pos0, s.W,
+                                       x["sink"], s.q_pos0, out, lse, dout, ws=ws)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / reps
+        kvb = 2 if s.kv == "bf16" else 4
+        rows = int((idx >= 0).sum()) + sum(min(s.W, s.q_pos0 + i + 1) for i in range(s.Lq))
+        nbytes = (rows * 2 * s.D * kvb + s.B * s.Lq * s.H * (3 * s.D * kvb + 4) + s.B * s.Lq * s.H * s.D * 4
+                  + 2 * s.B * (s.N_cap + s.T_raw) * s.D * 4)
+        res[name] = {"us": round(us, 1), "queries": s.B * s.Lq, "query_tok_s": round(s.B * s.Lq / (us * 1e-6), 1),
+                     "bytes": nbytes, "gbs": round(nbytes / us / 1e3, 1), "source_rows": rows}
+        main = (name, s, x, idx, dout)
+        del ws
+        torch.cuda.empty_cache()
+    name, s, x, idx, dout = main
+    m = res[name]
+    roof = {"bound": "hbm", "achieved": m["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(m["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "csa_sparse_attn_bwd (all launches of the call)", "bytes_per_launch": m["bytes"]}
+    result = {
+        "metric": "CSA attention backward query-tok/s (prefill chunk 4096 @64K, top-1024)",
+        "value": m["query_tok_s"], "unit": "query-tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(m["us"] / 1000.0, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) q, caches, dout; random sorted selections)",
+        "config": {"workload": "csa_attn_bwd_chunk4096_ctx64k", "cases": {c[0]: {"queries": c[1].B * c[1].Lq,
+                   "heads": c[1].H, "head_dim": c[1].D, "topk": c[1].topk, "window": c[1].W, "kv": c[1].kv}
+                   for c in cases}},
+        "roofline": roof, "cases": res,
+        "timing": "HIP events over back-to-back calls",
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _oracle_bwd_baseline(s, x, idx, dout, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _oracle_bwd_baseline(s, x, idx, dout, seconds):
+    """The oracle's per-query backward (attend_one_bwd) on query rows of the
+    workload until `seconds` of oracle work have run."""
+    import numpy as np
+    import torch
+    from oracle import attention_bwd as obwd, formats
+
+    def dec(t_):
+        t_ = t_.cpu()
+        if t_.dtype == torch.bfloat16:
+            return formats.bf16_to_f64(t_.view(torch.int16).numpy().view(np.uint16))
+        return t_.numpy().astype(np.float64)
+    sink = dec(x["sink"])
+    done, spent = 0, 0.0
+    while done < s.Lq and (done == 0 or spent < seconds):
+        i = s.Lq - 1 - done
+        t = s.q_pos0 + i
+        sel = idx[0, i][idx[0, i] >= 0]
+        lo = max(0, t - s.W + 1)
+        pos = np.arange(lo, t + 1)
+        rows = torch.from_numpy(sel.astype(np.int64)).to(x["k_c"].device)
+        q, kc, vc = dec(x["q"][0, i]), dec(x["k_c"][0][rows]), dec(x["v_c"][0][rows])
+        kr, vr = dec(x["k_raw"][0, lo - s.raw_pos0:t + 1 - s.raw_pos0]), dec(x["v_raw"][0, lo - s.raw_pos0:t + 1 - s.raw_pos0])
+        do = dec(dout[0, i])
+        t0 = time.perf_counter()
+        obwd.attend_one_bwd(q, t, kc, vc, kr, pos, vr, sink, do)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done / spent, 3), "unit": "query-tok/s", "cores": os.cpu_count(), "kind": "oracle",
+            "sample": "%d of %d query rows of csa_attn_bwd_chunk4096_ctx64k, %.1f s of oracle work (numpy float64)"
+                      % (done, s.Lq, spent)}
+
+
 def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
@@ -627,6 +735,9 @@ def main():
         return
     if W == "indexer_bf16_scores":
         bench_bf16_scores(args, torch, csa, wl, dev)
+        return
+    if W == "csa_attn_bwd":
+        bench_attn_bwd(args, torch, csa, wl, dev)
         return
     if W == "csa_decode":
         shapes = [("", wl.CFG2)]

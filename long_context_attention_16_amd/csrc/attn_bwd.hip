@@ -261,13 +261,20 @@ __global__ void fix_to_f32_kernel(const long long* acc, float* out, int64_t n) {
     out[i] = (float)((double)acc[i] * (1.0 / 4294967296.0));
 }
 
-// dsink[h] = sum over query rows, in row order (one thread per head).
-__global__ void dsink_sum_kernel(const float* part, int64_t rows, int H, float* dsink) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+// dsink[h] = sum over query rows in a fixed order: workgroup h, thread t
+// sums rows t, t + 256, ... in order, then a fixed tree over the threads.
+__global__ __launch_bounds__(256) void dsink_sum_kernel(const float* part, int64_t rows, int H, float* dsink) {
+  __shared__ float red[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
   float s = 0.f;
-  for (int64_t r = 0; r < rows; ++r) s += part[r * H + h];
-  dsink[h] = s;
+  for (int64_t r = tid; r < rows; r += 256) s += part[r * H + h];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) dsink[h] = red[0];
 }
 
 }  // namespace
@@ -315,7 +322,7 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int kv_dtype, const void* dout,
     hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_kr, dk_raw, nr);
     hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_vr, dv_raw, nr);
   }
-  if (dsink) hipLaunchKernelGGL(dsink_sum_kernel, dim3((a.H + 63) / 64), dim3(64), 0, st, g.dsink_part, rows, a.H, dsink);
+  if (dsink) hipLaunchKernelGGL(dsink_sum_kernel, dim3(a.H), dim3(256), 0, st, g.dsink_part, rows, a.H, dsink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
