@@ -495,7 +495,7 @@ def bench_attn_bwd(args, torch, csa, wl, dev):
         dout = torch.randn(x["q"].shape, generator=gen, device=dev).to(x["q"].dtype)
         out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], s.raw_pos0, s.W, x["sink"],
                                    s.q_pos0)
-        wsb = csa.attn_bwd_ws_bytes(s.B, s.Lq, s.H, s.D, s.N_cap, s.T_raw)
+        wsb = csa.attn_bwd_ws_bytes(s.B, s.Lq, s.q_pos0, 0, s.H, s.D, s.N_cap, s.topk, s.W)
         ws = torch.empty((wsb + 15) // 16 * 4, dtype=torch.float32, device=dev)
 
         def call():

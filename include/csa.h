@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum {
   CSA_F32 = 0,
@@ -372,9 +372,11 @@ int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int
  *   dsink_h = -sum over queries of exp(z_h - lse_h) Dl_h.
  * A row used by several queries (an entry selected by many queries of a
  * sequence, a raw row in many windows) receives the sum of their
- * contributions, accumulated as 64-bit integers in units of 2^-32 (exact,
- * so the result does not depend on the order; contributions are clamped to
- * |x| <= 2^30) and rounded once to float32.
+ * contributions. One workgroup owns each row and adds every contribution
+ * (each one a sum over heads in float32) as a 64-bit integer in units of
+ * 2^-32 (exact, so the result does not depend on the order; contributions
+ * are clamped to |x| <= 2^30), then rounds once to float32: no atomics on
+ * the gradients, the same bits on every call.
  *
  * Arguments of the forward call (uniform positions, linear raw rows), plus:
  *   out, lse    the forward's outputs ([B, Lq, H, D] in kv_dtype, [B, Lq, H] f32)
@@ -384,12 +386,19 @@ int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int
  *   dk_raw, dv_raw  [B, T_raw, D] float32, every row written (may be NULL
  *               when T_raw = 0)
  *   dsink       [H] float32 (required with a sink, else may be NULL)
- *   ws, ws_bytes  csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)
- *               bytes: 16 bytes per element of k_c, v_c, k_raw and v_raw plus
- *               the per-query sink parts; no initial contents needed.
+ *   ws, ws_bytes  csa_sparse_attn_bwd_ws_bytes(B, Lq, q_pos0, 0, H, D, N_cap,
+ *               topk, W) bytes (HCA: m instead of 0, topk 0); no initial
+ *               contents needed. It holds, per (query, source slot, head),
+ *               the weight P and dS / sqrt(D) (8 bytes; slots: topk + W for
+ *               CSA, n(q_pos0 + Lq - 1) + W for HCA), the rotated q, the sink
+ *               parts, and for CSA the index of the (query, slot) pairs of
+ *               each compressed entry (12 bytes per entry, 4 per pair).
+ * Errors: CSA_ERR_SHAPE also when B * Lq * topk >= 2^31 (pairs are indexed
+ * in 32 bits).
  * hca_dense_attn_bwd: the same for hca_dense_attn (block m, every visible entry).
  */
-size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int T_raw);
+size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int64_t N_cap, int topk,
+                                    int W);
 int csa_sparse_attn_bwd(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype,
                         const void* q, int64_t N_cap, const void* k_c, const void* v_c,
                         int topk, const int32_t* idx,

@@ -48,7 +48,7 @@ SIGNATURES = {
     "csa_index_topk_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I, _P, _P,
                                _Z, _P]),
     "csa_index_scores_ex": (_I, [_I, _I, _P, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P]),
-    "csa_sparse_attn_bwd_ws_bytes": (_Z, [_I, _I, _I, _I, _L, _I]),
+    "csa_sparse_attn_bwd_ws_bytes": (_Z, [_I, _I, _L, _I, _I, _I, _L, _I, _I]),
     "csa_sparse_attn_bwd": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "hca_dense_attn_bwd": (_I, [_I, _I, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _L, _P, _P, _I, _P, _P, _P, _P,
@@ -356,8 +356,9 @@ def index_scores_ex(q_i, w_i, k_i, q_pos0, m, fmt, score_dtype="bf16", q_pos=Non
 
 
 # ------------------------------------------------------------------ backward
-def attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw):
-    return lib().csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)
+def attn_bwd_ws_bytes(B, Lq, q_pos0, m, H, D, N_cap, topk, W):
+    """Workspace bytes of sparse_attn_bwd (m = 0) or hca_attn_bwd (m > 0, topk 0)."""
+    return lib().csa_sparse_attn_bwd_ws_bytes(B, Lq, q_pos0, m, H, D, N_cap, topk, W)
 
 
 def _bwd_outputs(q, k_c, k_raw, sink):
@@ -372,7 +373,7 @@ def sparse_attn_bwd(q, k_c, v_c, idx, k_raw, v_raw, raw_pos0, W, sink, q_pos0, o
     """Gradients of sparse_attn: (dq, dk_c, dv_c, dk_raw, dv_raw, dsink), f32."""
     B, Lq, H, D = q.shape
     if ws is None:
-        ws = _ws(attn_bwd_ws_bytes(B, Lq, H, D, k_c.shape[1], k_raw.shape[1]), q.device)
+        ws = _ws(attn_bwd_ws_bytes(B, Lq, q_pos0, 0, H, D, k_c.shape[1], idx.shape[-1], W), q.device)
     g = _bwd_outputs(q, k_c, k_raw, sink)
     _check(lib().csa_sparse_attn_bwd(B, Lq, q_pos0, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c), _ptr(v_c),
                                      idx.shape[-1], _ptr(idx), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W,
@@ -385,7 +386,7 @@ def hca_attn_bwd(q, k_c, v_c, m, k_raw, v_raw, raw_pos0, W, sink, q_pos0, out, l
     """Gradients of hca_attn: (dq, dk_c, dv_c, dk_raw, dv_raw, dsink), f32."""
     B, Lq, H, D = q.shape
     if ws is None:
-        ws = _ws(attn_bwd_ws_bytes(B, Lq, H, D, k_c.shape[1], k_raw.shape[1]), q.device)
+        ws = _ws(attn_bwd_ws_bytes(B, Lq, q_pos0, m, H, D, k_c.shape[1], 0, W), q.device)
     g = _bwd_outputs(q, k_c, k_raw, sink)
     _check(lib().hca_dense_attn_bwd(B, Lq, q_pos0, m, H, D, _kv_dtype(q), _ptr(q), k_c.shape[1], _ptr(k_c),
                                     _ptr(v_c), k_raw.shape[1], raw_pos0, _ptr(k_raw), _ptr(v_raw), W, _ptr(sink),

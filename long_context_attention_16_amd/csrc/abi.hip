@@ -396,9 +396,18 @@ int hca_dense_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_max
                     out, lse, ws, ws_bytes, stream);
 }
 
-size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int T_raw) {
-  if (B <= 0 || Lq <= 0 || H <= 0 || D <= 0 || N_cap < 0 || T_raw < 0) return 16;
-  return attn_bwd_ws_bytes(B, Lq, H, N_cap, T_raw, D);
+// Source slots per query row of the backward: the selected entries (CSA) or
+// the entries visible to the last query (HCA, m > 0), then the window.
+static int64_t bwd_slots(int Lq, int64_t q_pos0, int m, int topk, int W) {
+  return (m > 0 ? n_last(q_pos0, Lq, m) : (int64_t)topk) + W;
+}
+
+size_t csa_sparse_attn_bwd_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int64_t N_cap, int topk,
+                                    int W) {
+  if (B <= 0 || Lq <= 0 || q_pos0 < 0 || m < 0 || H <= 0 || D <= 0 || N_cap < 0 || topk < 0 || W < 0) return 16;
+  const int64_t S = bwd_slots(Lq, q_pos0, m, topk, W);
+  if (S > (1 << 30)) return 16;
+  return attn_bwd_ws_bytes(B, Lq, H, D, N_cap, (int)S, m > 0 ? 0 : topk);
 }
 
 // csa_sparse_attn_bwd and hca_dense_attn_bwd (m > 0: HCA, every visible entry).
@@ -418,13 +427,17 @@ static int attn_bwd(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_d
   if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk_c) || !aligned16(dv_c) ||
       (T_raw > 0 && (!aligned16(dk_raw) || !aligned16(dv_raw))))
     return CSA_ERR_ALIGN;
-  if (!ws || ws_bytes < csa_sparse_attn_bwd_ws_bytes(B, Lq, H, D, N_cap, T_raw)) return CSA_ERR_WORKSPACE;
+  // pairs are indexed as qrow * topk + slot in 32 bits
+  if (!hca && (int64_t)B * Lq * topk >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
+  const int64_t S = bwd_slots(Lq, q_pos0, m, topk, W);
+  if (!ws || ws_bytes < csa_sparse_attn_bwd_ws_bytes(B, Lq, q_pos0, m, H, D, N_cap, topk, W))
+    return CSA_ERR_WORKSPACE;
   AttnArgs a{};
   a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.m = hca ? m : 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
   a.k_c = k_c; a.v_c = v_c; a.topk = hca ? 0 : topk; a.idx = hca ? nullptr : idx; a.T_raw = T_raw;
   a.raw_pos0 = raw_pos0; a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = (void*)out;
   a.lse = (float*)lse;
-  return launch_attn_bwd(a, hca, kv_dtype, dout, dq, dk_c, dv_c, dk_raw, dv_raw, dsink, ws, as_stream(stream))
+  return launch_attn_bwd(a, hca, (int)S, kv_dtype, dout, dq, dk_c, dv_c, dk_raw, dv_raw, dsink, ws, as_stream(stream))
              ? CSA_ERR_LAUNCH : CSA_OK;
 }
 

@@ -12,15 +12,23 @@
 //   dk_r = sum_h dS_hr RoPE(q_h, t) / sqrt(D)  (window rows: RoPE^T at s);
 //   dv_r = sum_h P_hr dO_h;  dz_h = -exp(z_h - lse_h) Dl_h.
 //
-// Design. Workgroup = (query row, group of 4 heads): the query's source rows
-// go through LDS in tiles of 8 (f32, window keys rotated in LDS), logits and
-// dP by 4 threads per dot product, dq accumulated in registers. A row's key
-// and value gradients receive contributions from every query (and head
-// group) that uses it; they are added as 64-bit fixed-point integers
-// (units of 2^-32) with atomics, so the sums are exact and the result is the
-// same bits whatever the order of the additions: deterministic without a
-// split-free ordering pass. A last kernel converts them to f32; the sinks'
-// per-query parts are summed in query order.
+// Design, in three parts.
+//  * Query pass, workgroup = (query row, group of 4 heads): the query's
+//    source rows go through LDS in tiles of 8 (f32, window keys rotated in
+//    LDS), logits and dP by 4 threads per dot product, dq accumulated in
+//    registers. It writes, for every (query, source slot, head), P and
+//    dS / sqrt(D), and the rotated q, for the second part.
+//  * Inverse index (CSA): the (query, slot) pairs that select each
+//    compressed entry, grouped by entry (counts, a scan, a fill). HCA entries
+//    and window rows need none: the queries that use them form a range.
+//  * Key/value pass, workgroup = one compressed entry or one raw row: it
+//    walks the row's pairs and sums dk = sum dS RoPE(q) / sqrt(D) and
+//    dv = sum P dO over them, each pair's value (over heads, in f32) added
+//    to a 64-bit fixed-point accumulator (units of 2^-32) held in
+//    registers. Integer sums are exact, so the result is the same bits in
+//    whatever order the pairs are listed: deterministic with no atomics on
+//    the gradients and no ordering pass. Window rows are rotated back.
+// The sinks' per-query parts are summed in query order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,16 +37,40 @@ namespace csa {
 namespace {
 
 constexpr int kBwdThreads = 256;
-constexpr int kBwdHeads = 4;   // heads per workgroup
+constexpr int kBwdHeads = 4;   // heads per query-pass workgroup
 constexpr int kBwdRows = 8;    // source rows per tile
+constexpr int kKvThreads = 256;
+constexpr int kKvWaves = kKvThreads / kWave;
+constexpr int kKvList = 1024;  // pairs of an entry staged in LDS at once
+constexpr int kScanBlock = 4096;  // counts per scan block (256 threads x 16)
 constexpr float kFixScale = 4294967296.f;  // 2^32: fixed-point unit 2^-32
+
+// Workspace pieces (attn_bwd_ws_bytes), each 256-byte aligned.
+struct BwdWs {
+  float2* pds;        // [rows][S][H]: (P, dS / sqrt(D)) of each (query, source slot, head)
+  void* qr;           // [rows][H][D] RoPE(q, t) in the KV dtype
+  float* dsink_part;  // [rows][H]
+  int *cnt, *cur;     // [E = B * N_cap]: selections of each compressed entry; fill cursors
+  int* off;           // [E] exclusive offsets within the entry's scan block
+  int* bsum;          // [ceil(E / kScanBlock)] block totals, then their exclusive offsets
+  int* list;          // [rows * topk] flat pair index qrow * topk + slot, grouped by entry
+};
 
 struct AttnBwdArgs {
   AttnArgs a;
+  int S;  // source slots per query row (pds stride): topk + W (CSA), n(t_last) + W (HCA)
   const void* dout;
   float* dq;
-  long long *acc_kc, *acc_vc, *acc_kr, *acc_vr;
-  float* dsink_part;  // [B*Lq][H]
+  BwdWs w;
+};
+
+struct BwdKvArgs {
+  AttnArgs a;
+  int S;
+  int listed;  // CSA with at least one pair: the inverse index is built
+  const void* dout;
+  BwdWs w;
+  float *dk_c, *dv_c, *dk_raw, *dv_raw;
 };
 
 __device__ __forceinline__ long long to_fix(float x) {
@@ -49,6 +81,41 @@ __device__ __forceinline__ long long to_fix(float x) {
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) {
   return Elem<T>::load(p + i);
+}
+
+// N consecutive elements of T at p (N * sizeof(T) bytes, aligned to that size
+// up to 16) as floats.
+template <typename T, int N>
+__device__ __forceinline__ void ld_vec(const T* p, float* o) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(N % 2 == 0, "bf16 pairs");
+    uint32_t w[N / 2];
+    if constexpr (N == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p + 8 * i);
+        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    if constexpr (N == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      o[0] = v.x; o[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < N / 4; ++i) {
+        const float4 v = *reinterpret_cast<const float4*>(p + 4 * i);
+        o[4 * i] = v.x; o[4 * i + 1] = v.y; o[4 * i + 2] = v.z; o[4 * i + 3] = v.w;
+      }
+    }
+  }
 }
 
 // Source row sp of query row qrow: kind 0 masked, 1 compressed entry j, 2
@@ -72,15 +139,17 @@ __device__ __forceinline__ int bwd_source(const AttnArgs& p, int b, int64_t qrow
   return 2;
 }
 
+// Query pass: dq, the rotated q, (P, dS / sqrt(D)) of every source slot and
+// the query's sink parts.
 template <typename T, int D, bool HCA>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
+__global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) {
   const AttnArgs& p = g.a;
   constexpr int NT = kBwdThreads, HG = kBwdHeads, R = kBwdRows;
   constexpr int EPT = HG * D / NT;  // (head, d) elements of a thread: e = tid + NT * k
   static_assert(EPT >= 1 && HG * D % NT == 0, "whole elements per thread");
   __shared__ float s_q[HG][D], s_do[HG][D];
   __shared__ float s_k[R][D], s_v[R][D];
-  __shared__ float s_l[HG][R], s_dp[HG][R], s_p[HG][R], s_ds[HG][R];
+  __shared__ float s_l[HG][R], s_dp[HG][R], s_ds[HG][R];
   __shared__ float s_lse[HG], s_dl[HG];
   __shared__ int s_kind[R];
   __shared__ int64_t s_row[R], s_pos[R];
@@ -129,13 +198,22 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
     if (part == 0) s_dl[hh] = acc;
   }
   __syncthreads();
+  // the rotated q for the key/value pass
+  T* qrb = (T*)g.w.qr + (qrow * p.H) * D;
+  for (int e = tid; e < HG * D; e += NT) {
+    const int hh = e / D, d = e % D, h = h0 + hh;
+    if (h < p.H) Elem<T>::store(qrb + (int64_t)h * D + d, s_q[hh][d]);
+  }
 
   float dq[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) dq[k] = 0.f;
 
+  float2* pdq = g.w.pds + qrow * (int64_t)g.S * p.H;
   for (int r0 = 0; r0 < S; r0 += R) {
-    // the tile's rows: sources, then K (window rows rotated at their position) and V
+    // The tile's rows: sources (the previous tile's last readers of s_kind
+    // and s_row passed the barrier before its dq update, which reads only
+    // s_ds and s_k), then K (window rows rotated at their position) and V.
     if (tid < R) {
       int64_t row, pos;
       s_kind[tid] = r0 + tid < S ? bwd_source<HCA>(p, b, qrow, n_c, lo, n_w, r0 + tid, &row, &pos) : 0;
@@ -162,8 +240,8 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
     }
     __syncthreads();
     // logits (dot < HG*R) and dP (the rest): 4 threads per dot product
-    {
-      const int dot = tid / 4, part = tid % 4;
+    for (int dot = tid / 4; dot < 2 * HG * R; dot += NT / 4) {
+      const int part = tid % 4;
       const int hh = (dot % (HG * R)) / R, r = dot % R;
       const bool is_l = dot < HG * R;
       float acc = 0.f;
@@ -181,8 +259,9 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
       const int hh = tid / R, r = tid % R;
       const bool ok = s_kind[r] != 0 && h0 + hh < p.H;
       const float pv = ok ? __expf(s_l[hh][r] - s_lse[hh]) : 0.f;
-      s_p[hh][r] = pv;
-      s_ds[hh][r] = ok ? pv * (s_dp[hh][r] - s_dl[hh]) : 0.f;
+      const float ds = ok ? pv * (s_dp[hh][r] - s_dl[hh]) : 0.f;
+      s_ds[hh][r] = ds;
+      if (r0 + r < S && h0 + hh < p.H) pdq[(int64_t)(r0 + r) * p.H + h0 + hh] = make_float2(pv, ds * rs);
     }
     __syncthreads();
     // dq += dS k (unscaled; 1/sqrt(D) at the end)
@@ -192,39 +271,8 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
 #pragma unroll
       for (int r = 0; r < R; ++r) dq[k] = fmaf(s_ds[hh][r], s_k[r][d], dq[k]);
     }
-    __syncthreads();  // every thread is done with s_k: reuse it for the key gradients
-    for (int e = tid; e < R * D; e += NT) {
-      const int r = e / D, d = e % D;
-      float u = 0.f, w = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < HG; ++hh) {
-        u = fmaf(s_ds[hh][r], s_q[hh][d], u);
-        w = fmaf(s_p[hh][r], s_do[hh][d], w);
-      }
-      s_k[r][d] = u * rs;
-      s_v[r][d] = w;
-    }
-    __syncthreads();
-    for (int e = tid; e < R * kRopePairs; e += NT) {  // window rows: back to the unrotated frame
-      const int r = e / kRopePairs, pr = e % kRopePairs, d = D - kRopeDims + 2 * pr;
-      if (s_kind[r] != 2) continue;
-      float c, sn;
-      rope_cos_sin(s_pos[r], pr, &c, &sn);
-      const float x0 = s_k[r][d], x1 = s_k[r][d + 1];
-      s_k[r][d] = x0 * c + x1 * sn;
-      s_k[r][d + 1] = -x0 * sn + x1 * c;
-    }
-    __syncthreads();
-    for (int e = tid; e < R * D; e += NT) {
-      const int r = e / D, d = e % D, kd = s_kind[r];
-      if (!kd) continue;
-      long long* ak = kd == 2 ? g.acc_kr : g.acc_kc;
-      long long* av = kd == 2 ? g.acc_vr : g.acc_vc;
-      atomicAdd((unsigned long long*)(ak + s_row[r] * D + d), (unsigned long long)to_fix(s_k[r][d]));
-      atomicAdd((unsigned long long*)(av + s_row[r] * D + d), (unsigned long long)to_fix(s_v[r][d]));
-    }
-    __syncthreads();  // the tile's LDS is reused by the next tile
   }
+  __syncthreads();  // every thread is done with s_q's last reader above (none) and s_k
 
   // dq: back to the unrotated frame (pairs in LDS), scaled by 1/sqrt(D)
 #pragma unroll
@@ -248,17 +296,242 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(AttnBwdArgs g) {
   }
   if (tid < HG && h0 + tid < p.H) {
     const int h = h0 + tid;
-    g.dsink_part[qrow * p.H + h] = p.sink ? -__expf(p.sink[h] - s_lse[tid]) * s_dl[tid] : 0.f;
+    g.w.dsink_part[qrow * p.H + h] = p.sink ? -__expf(p.sink[h] - s_lse[tid]) * s_dl[tid] : 0.f;
   }
 }
 
-__global__ void fill_zero_kernel(long long* p, int64_t n) {
+// ------------------------------------------------------ inverse index (CSA)
+__global__ void bwd_zero_kernel(int* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-__global__ void fix_to_f32_kernel(const long long* acc, float* out, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = (float)((double)acc[i] * (1.0 / 4294967296.0));
+// Entry of flat pair pi (= qrow * topk + slot), or -1 when the slot is masked.
+__device__ __forceinline__ int64_t pair_entry(const AttnArgs& p, int64_t pi) {
+  const int32_t j = p.idx[pi];
+  if (j < 0 || j >= p.N_cap) return -1;
+  const int64_t b = pi / p.topk / p.Lq;
+  return b * p.N_cap + j;
+}
+
+__global__ void bwd_count_kernel(AttnArgs p, int64_t npairs, int* cnt) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = pair_entry(p, i);
+    if (e >= 0) atomicAdd(cnt + e, 1);
+  }
+}
+
+// Exclusive scan of 256 per-thread values in LDS (Hillis-Steele); returns
+// this thread's exclusive prefix and *total.
+__device__ __forceinline__ int scan256(int v, int* buf, int* total) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int x = tid >= o ? buf[tid - o] : 0;
+    __syncthreads();
+    buf[tid] += x;
+    __syncthreads();
+  }
+  const int inc = buf[tid];
+  *total = buf[255];
+  __syncthreads();
+  return inc - v;
+}
+
+// off[e] = exclusive prefix of cnt within its block of kScanBlock entries;
+// bsum[block] = the block's total.
+__global__ __launch_bounds__(256) void bwd_scan_block_kernel(const int* cnt, int64_t E, int* off, int* bsum) {
+  __shared__ int buf[256];
+  constexpr int PER = kScanBlock / 256;
+  const int64_t e0 = (int64_t)blockIdx.x * kScanBlock + threadIdx.x * PER;
+  int v[PER], s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    v[i] = e0 + i < E ? cnt[e0 + i] : 0;
+    s += v[i];
+  }
+  int total;
+  int run = scan256(s, buf, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (e0 + i < E) off[e0 + i] = run;
+    run += v[i];
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// bsum[0..n) -> exclusive prefix sums, one workgroup, 256 at a time.
+__global__ __launch_bounds__(256) void bwd_scan_top_kernel(int* bsum, int n) {
+  __shared__ int buf[256];
+  int carry = 0;
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    const int i = c0 + threadIdx.x;
+    const int v = i < n ? bsum[i] : 0;
+    int total;
+    const int ex = scan256(v, buf, &total);
+    if (i < n) bsum[i] = carry + ex;
+    carry += total;
+  }
+}
+
+__global__ void bwd_fill_kernel(AttnArgs p, int64_t npairs, const int* off, const int* bsum, int* cur, int* list) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = pair_entry(p, i);
+    if (e >= 0) list[off[e] + bsum[e / kScanBlock] + atomicAdd(cur + e, 1)] = (int)i;
+  }
+}
+
+// ------------------------------------------------------- key/value pass
+// Workgroup = one compressed entry (blocks [0, B * N_cap)) or one raw row
+// (the rest). Wave w takes pairs w*U.. of every kKvWaves*U; lane l owns the
+// VPT consecutive dims l*VPT.. of the row.
+template <typename T, int D, bool HCA>
+__global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(BwdKvArgs g) {
+  constexpr int VPT = D / kWave;
+  constexpr int U = VPT <= 2 ? 4 : 2;  // pairs in flight per wave
+  constexpr int HC = 4;                 // heads per inner step
+  const AttnArgs& p = g.a;
+  __shared__ int s_list[kKvList];
+  __shared__ long long s_acc[kKvWaves - 1][2][D];
+
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int64_t ecount = (int64_t)p.B * p.N_cap;
+  const int64_t blk = blockIdx.x;
+  const bool win = blk >= ecount;
+  const int b = (int)(win ? (blk - ecount) / p.T_raw : blk / p.N_cap);
+  const int64_t r = win ? (blk - ecount) % p.T_raw : blk % p.N_cap;
+  const int64_t s_pos = p.raw_pos0 + r;  // window rows: absolute position
+  // The row's pairs: CSA entries from the list, else the query range [i0, i0 + n).
+  int64_t n = 0, start = 0, i0 = 0;
+  if (win) {
+    if (p.W > 0) {
+      const int64_t a0 = s_pos - p.q_pos0, a1 = s_pos + p.W - 1 - p.q_pos0;
+      i0 = a0 > 0 ? a0 : 0;
+      const int64_t i1 = a1 < p.Lq - 1 ? a1 : p.Lq - 1;
+      n = i1 >= i0 ? i1 - i0 + 1 : 0;
+    }
+  } else if (HCA) {
+    const int64_t a0 = (r + 1) * p.m - 1 - p.q_pos0;
+    i0 = a0 > 0 ? a0 : 0;
+    n = p.Lq > i0 ? p.Lq - i0 : 0;
+  } else if (g.listed) {
+    n = g.w.cnt[blk];
+    start = g.w.off[blk] + g.w.bsum[blk / kScanBlock];
+  }
+  const bool listed = !win && !HCA;
+
+  long long ak[VPT], av[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) ak[v] = av[v] = 0;
+  const T* qr = (const T*)g.w.qr;
+  const T* dout = (const T*)g.dout;
+  const int d0 = lane * VPT;
+
+  for (int64_t c0 = 0; c0 < n; c0 += kKvList) {
+    const int cn = (int)(n - c0 < kKvList ? n - c0 : kKvList);
+    if (listed) {
+      __syncthreads();  // the previous chunk's readers are done
+      for (int i = tid; i < cn; i += kKvThreads) s_list[i] = g.w.list[start + c0 + i];
+      __syncthreads();
+    }
+    for (int k = wave * U; k < cn; k += kKvWaves * U) {
+      int64_t qrow[U], slot[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        ok[u] = k + u < cn;
+        const int kk = ok[u] ? k + u : k;
+        if (listed) {
+          const int pi = __builtin_amdgcn_readfirstlane(s_list[kk]);
+          qrow[u] = pi / p.topk;
+          slot[u] = pi - qrow[u] * p.topk;
+        } else {
+          const int64_t i = i0 + c0 + kk;
+          qrow[u] = (int64_t)b * p.Lq + i;
+          if (win) {
+            const int64_t t = p.q_pos0 + i;
+            const int64_t lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;
+            slot[u] = (HCA ? (t + 1) / p.m : p.topk) + (s_pos - lo);
+          } else {
+            slot[u] = r;
+          }
+        }
+      }
+      float uk[U][VPT], uv[U][VPT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) uk[u][v] = uv[u][v] = 0.f;
+      for (int h0 = 0; h0 < p.H; h0 += HC) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float2* pd = g.w.pds + (qrow[u] * g.S + slot[u]) * p.H;
+#pragma unroll
+          for (int hh = 0; hh < HC; ++hh) {
+            const int h = h0 + hh;
+            if (h < p.H) {
+              const float2 w2 = pd[h];
+              float xq[VPT], xo[VPT];
+              ld_vec<T, VPT>(qr + (qrow[u] * p.H + h) * D + d0, xq);
+              ld_vec<T, VPT>(dout + (qrow[u] * p.H + h) * D + d0, xo);
+#pragma unroll
+              for (int v = 0; v < VPT; ++v) {
+                uk[u][v] = fmaf(w2.y, xq[v], uk[u][v]);
+                uv[u][v] = fmaf(w2.x, xo[v], uv[u][v]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ok[u])
+#pragma unroll
+          for (int v = 0; v < VPT; ++v) {
+            ak[v] += to_fix(uk[u][v]);
+            av[v] += to_fix(uv[u][v]);
+          }
+    }
+  }
+
+  // the waves' sums (exact integers, any order), converted and written by wave 0
+  if (wave > 0)
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      s_acc[wave - 1][0][d0 + v] = ak[v];
+      s_acc[wave - 1][1][d0 + v] = av[v];
+    }
+  __syncthreads();
+  if (wave != 0) return;
+  float fk[VPT], fv[VPT];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+#pragma unroll
+    for (int w = 0; w < kKvWaves - 1; ++w) {
+      ak[v] += s_acc[w][0][d0 + v];
+      av[v] += s_acc[w][1][d0 + v];
+    }
+    fk[v] = (float)((double)ak[v] * (1.0 / 4294967296.0));
+    fv[v] = (float)((double)av[v] * (1.0 / 4294967296.0));
+  }
+  if (win && d0 >= D - kRopeDims) {  // window keys: back to the unrotated frame
+#pragma unroll
+    for (int v = 0; v < VPT; v += 2) {
+      float c, sn;
+      rope_cos_sin(s_pos, (d0 + v - (D - kRopeDims)) / 2, &c, &sn);
+      const float x0 = fk[v], x1 = fk[v + 1];
+      fk[v] = x0 * c + x1 * sn;
+      fk[v + 1] = -x0 * sn + x1 * c;
+    }
+  }
+  float* ok_ = win ? g.dk_raw + ((int64_t)b * p.T_raw + r) * D : g.dk_c + ((int64_t)b * p.N_cap + r) * D;
+  float* ov_ = win ? g.dv_raw + ((int64_t)b * p.T_raw + r) * D : g.dv_c + ((int64_t)b * p.N_cap + r) * D;
+#pragma unroll
+  for (int v = 0; v < VPT; v += 2) {
+    *reinterpret_cast<float2*>(ok_ + d0 + v) = make_float2(fk[v], fk[v + 1]);
+    *reinterpret_cast<float2*>(ov_ + d0 + v) = make_float2(fv[v], fv[v + 1]);
+  }
 }
 
 // dsink[h] = sum over query rows in a fixed order: workgroup h, thread t
@@ -277,34 +550,71 @@ __global__ __launch_bounds__(256) void dsink_sum_kernel(const float* part, int64
   if (tid == 0) dsink[h] = red[0];
 }
 
-}  // namespace
+inline size_t al256(size_t n) { return (n + 255) / 256 * 256; }
 
-size_t attn_bwd_ws_bytes(int B, int Lq, int H, int64_t N_cap, int T_raw, int D) {
-  const size_t acc = ((size_t)B * N_cap + (size_t)B * T_raw) * D * 2 * sizeof(long long);
-  return acc + ((size_t)B * Lq * H * sizeof(float) + 255) / 256 * 256;
+struct BwdSizes {
+  size_t pds, qr, sink, cnt, off, bsum, list;
+  size_t total() const { return pds + qr + sink + 2 * cnt + off + bsum + list; }
+};
+
+BwdSizes bwd_sizes(int B, int Lq, int H, int D, int64_t N_cap, int S, int topk) {
+  const size_t rows = (size_t)B * Lq, E = topk > 0 ? (size_t)B * N_cap : 0;
+  BwdSizes z;
+  z.pds = al256(rows * S * H * sizeof(float2));
+  z.qr = al256(rows * H * D * sizeof(float));  // room for f32 q
+  z.sink = al256(rows * H * sizeof(float));
+  z.cnt = al256(E * sizeof(int));
+  z.off = al256(E * sizeof(int));
+  z.bsum = al256((E + kScanBlock - 1) / kScanBlock * sizeof(int));
+  z.list = al256(rows * (size_t)topk * sizeof(int));
+  return z;
 }
 
-int launch_attn_bwd(const AttnArgs& a, bool hca, int kv_dtype, const void* dout, float* dq, float* dk_c, float* dv_c,
-                    float* dk_raw, float* dv_raw, float* dsink, void* ws, hipStream_t st) {
-  AttnBwdArgs g;
-  g.a = a;
-  g.dout = dout;
-  g.dq = dq;
-  const int64_t nc = (int64_t)a.B * a.N_cap * a.D, nr = (int64_t)a.B * a.T_raw * a.D;
-  g.acc_kc = (long long*)ws;
-  g.acc_vc = g.acc_kc + nc;
-  g.acc_kr = g.acc_vc + nc;
-  g.acc_vr = g.acc_kr + nr;
-  g.dsink_part = (float*)(g.acc_vr + nr);
-  const int64_t nacc = 2 * (nc + nr);
-  const int fill_blocks = (int)((nacc + 255) / 256 < 4096 ? (nacc + 255) / 256 : 4096);
-  if (nacc > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3(fill_blocks), dim3(256), 0, st, g.acc_kc, nacc);
+}  // namespace
+
+size_t attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int S, int topk) {
+  return bwd_sizes(B, Lq, H, D, N_cap, S, topk).total() + 256;
+}
+
+int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void* dout, float* dq, float* dk_c,
+                    float* dv_c, float* dk_raw, float* dv_raw, float* dsink, void* ws, hipStream_t st) {
+  const BwdSizes z = bwd_sizes(a.B, a.Lq, a.H, a.D, a.N_cap, S, hca ? 0 : a.topk);
+  uint8_t* w8 = (uint8_t*)ws;
+  BwdWs w;
+  w.pds = (float2*)w8;             w8 += z.pds;
+  w.qr = w8;                       w8 += z.qr;
+  w.dsink_part = (float*)w8;       w8 += z.sink;
+  w.cnt = (int*)w8;                w8 += z.cnt;
+  w.cur = (int*)w8;                w8 += z.cnt;
+  w.off = (int*)w8;                w8 += z.off;
+  w.bsum = (int*)w8;               w8 += z.bsum;
+  w.list = (int*)w8;
   const int64_t rows = (int64_t)a.B * a.Lq;
+  const int64_t E = (int64_t)a.B * a.N_cap;
+  const int64_t npairs = rows * a.topk;
+  // inverse index of the selections (CSA)
+  if (!hca && npairs > 0) {
+    const int64_t nz = (int64_t)(2 * z.cnt / sizeof(int));
+    const int zb = (int)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(zb), dim3(256), 0, st, w.cnt, nz);
+    const int pb = (int)((npairs + 255) / 256 < 4096 ? (npairs + 255) / 256 : 4096);
+    hipLaunchKernelGGL(bwd_count_kernel, dim3(pb), dim3(256), 0, st, a, npairs, w.cnt);
+    const int nblk = (int)((E + kScanBlock - 1) / kScanBlock);
+    hipLaunchKernelGGL(bwd_scan_block_kernel, dim3(nblk), dim3(256), 0, st, w.cnt, E, w.off, w.bsum);
+    hipLaunchKernelGGL(bwd_scan_top_kernel, dim3(1), dim3(256), 0, st, w.bsum, nblk);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(pb), dim3(256), 0, st, a, npairs, w.off, w.bsum, w.cur, w.list);
+  }
   if (rows > 0) {
+    AttnBwdArgs g;
+    g.a = a;
+    g.S = S;
+    g.dout = dout;
+    g.dq = dq;
+    g.w = w;
     const dim3 grid((unsigned)(rows * ((a.H + kBwdHeads - 1) / kBwdHeads)));
 #define CSA_BWD(TT, DD)                                                                                    \
-  if (hca) hipLaunchKernelGGL((attn_bwd_kernel<TT, DD, true>), grid, dim3(kBwdThreads), 0, st, g);        \
-  else hipLaunchKernelGGL((attn_bwd_kernel<TT, DD, false>), grid, dim3(kBwdThreads), 0, st, g)
+  if (hca) hipLaunchKernelGGL((attn_bwd_q_kernel<TT, DD, true>), grid, dim3(kBwdThreads), 0, st, g);      \
+  else hipLaunchKernelGGL((attn_bwd_q_kernel<TT, DD, false>), grid, dim3(kBwdThreads), 0, st, g)
     if (kv_dtype == 0) {
       if (a.D == 128) { CSA_BWD(float, 128); } else { CSA_BWD(float, 512); }
     } else {
@@ -312,17 +622,27 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int kv_dtype, const void* dout,
     }
 #undef CSA_BWD
   }
-  if (nc > 0) {
-    const int nb = (int)((nc + 255) / 256 < 4096 ? (nc + 255) / 256 : 4096);
-    hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_kc, dk_c, nc);
-    hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_vc, dv_c, nc);
+  const int64_t kv_blocks = E + (int64_t)a.B * a.T_raw;
+  if (kv_blocks > 0) {
+    BwdKvArgs g;
+    g.a = a;
+    g.S = S;
+    g.listed = !hca && npairs > 0;
+    g.dout = dout;
+    g.w = w;
+    g.dk_c = dk_c; g.dv_c = dv_c; g.dk_raw = dk_raw; g.dv_raw = dv_raw;
+    const dim3 grid((unsigned)kv_blocks);
+#define CSA_BWD_KV(TT, DD)                                                                                  \
+  if (hca) hipLaunchKernelGGL((attn_bwd_kv_kernel<TT, DD, true>), grid, dim3(kKvThreads), 0, st, g);      \
+  else hipLaunchKernelGGL((attn_bwd_kv_kernel<TT, DD, false>), grid, dim3(kKvThreads), 0, st, g)
+    if (kv_dtype == 0) {
+      if (a.D == 128) { CSA_BWD_KV(float, 128); } else { CSA_BWD_KV(float, 512); }
+    } else {
+      if (a.D == 128) { CSA_BWD_KV(uint16_t, 128); } else { CSA_BWD_KV(uint16_t, 512); }
+    }
+#undef CSA_BWD_KV
   }
-  if (nr > 0) {
-    const int nb = (int)((nr + 255) / 256 < 4096 ? (nr + 255) / 256 : 4096);
-    hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_kr, dk_raw, nr);
-    hipLaunchKernelGGL(fix_to_f32_kernel, dim3(nb), dim3(256), 0, st, g.acc_vr, dv_raw, nr);
-  }
-  if (dsink) hipLaunchKernelGGL(dsink_sum_kernel, dim3(a.H), dim3(256), 0, st, g.dsink_part, rows, a.H, dsink);
+  if (dsink && rows > 0) hipLaunchKernelGGL(dsink_sum_kernel, dim3(a.H), dim3(256), 0, st, w.dsink_part, rows, a.H, dsink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

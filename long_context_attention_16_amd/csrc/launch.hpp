@@ -108,10 +108,11 @@ size_t topk_ws_bytes(int B, int Lq, int64_t n_max, int topk);
 int launch_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, const float* scores,
                 int sbf, int topk, int32_t* idx_out, void* ws, hipStream_t stream);
 int launch_attn(const AttnArgs& a, int kv_dtype, bool hca, hipStream_t stream);
-// Attention backward (attn_bwd.hip): fixed-point accumulators and per-query
-// sink parts in ws (attn_bwd_ws_bytes).
-size_t attn_bwd_ws_bytes(int B, int Lq, int H, int64_t N_cap, int T_raw, int D);
-int launch_attn_bwd(const AttnArgs& a, bool hca, int kv_dtype, const void* dout, float* dq, float* dk_c, float* dv_c,
-                    float* dk_raw, float* dv_raw, float* dsink, void* ws, hipStream_t st);
+// Attention backward (attn_bwd.hip). S = source slots per query row (topk +
+// W for CSA, n(t_last) + W for HCA); ws holds the per-slot weights, the
+// rotated q, the sink parts and the inverse index (attn_bwd_ws_bytes).
+size_t attn_bwd_ws_bytes(int B, int Lq, int H, int D, int64_t N_cap, int S, int topk);
+int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void* dout, float* dq, float* dk_c,
+                    float* dv_c, float* dk_raw, float* dv_raw, float* dsink, void* ws, hipStream_t st);
 
 }  // namespace csa

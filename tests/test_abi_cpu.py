@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for code in range(7):
         assert len(lib.csa_strerror(code)) > 0
     assert lib.csa_strerror(99) == b"unknown status"
@@ -206,7 +206,7 @@ def test_index_topk_ex_rejects(lib):
 
 def test_attn_bwd_rejects(lib):
     f = lib.csa_sparse_attn_bwd
-    n = lib.csa_sparse_attn_bwd_ws_bytes(1, 1, 4, 128, 64, 8)
+    n = lib.csa_sparse_attn_bwd_ws_bytes(1, 1, 100, 0, 4, 128, 64, 16, 8)
     base = [1, 1, 100, 4, 128, 1, P, 64, P, P, 16, P, 8, 93, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n, None]
     bad = list(base); bad[13] = 94
     assert f(*bad) == SHAPE                       # window row 93 not covered
@@ -218,6 +218,9 @@ def test_attn_bwd_rejects(lib):
     assert f(*bad) == WS
     bad = list(base); bad[21] = MIS
     assert f(*bad) == ALIGN                       # dq
+    bad = list(base); bad[1] = 1 << 21; bad[10] = 1024; bad[16] = 0
+    assert f(*bad) == SHAPE                       # B * Lq * topk pairs exceed 32-bit indices
+    assert lib.csa_sparse_attn_bwd_ws_bytes(1, 1, 100, 0, 4, 128, 64, 32, 8) > n    # more slots, larger
     h = lib.hca_dense_attn_bwd
     hb = [1, 1, 1000, 128, 4, 128, 1, P, 6, P, P, 8, 993, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n, None]
     assert h(*hb) == SHAPE                        # n(1000) = 7 entries need N_cap >= 7

@@ -125,3 +125,30 @@ def test_bwd_deterministic_and_batch_invariant():
         assert torch.equal(a, b)
     for a, b in zip(g1[:5], g3[:5]):
         assert torch.equal(a[:1], b)
+
+
+def test_sparse_attn_bwd_hot_entry_and_duplicates():
+    """Entries 0 and 1 selected by every one of 1100 queries (more pairs than
+    the key/value pass stages at once), and queries that list an entry twice
+    (two slots, two contributions)."""
+    fmt, B, Lq, H, D, k, W, q_pos0, m = "f32", 1, 1100, 4, 128, 6, 4, 64, 4
+    N_cap = (q_pos0 + Lq) // m + 1
+    raw_pos0 = q_pos0 - W
+    T_raw = q_pos0 + Lq - raw_pos0
+    x = _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=5)
+    rng = np.random.default_rng(12)
+    idx = np.full((B, Lq, k), -1, dtype=np.int32)
+    for i in range(Lq):
+        n = (q_pos0 + i + 1) // m
+        idx[0, i, :2] = [0, 1]
+        idx[0, i, 2:5] = rng.choice(np.arange(2, n), size=3, replace=False)
+        idx[0, i, 5] = idx[0, i, 2] if i % 7 == 0 else -1
+    it = torch.from_numpy(idx).to(DEV)
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0)
+    g = csa.sparse_attn_bwd(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0,
+                            out, lse, x["dout"])
+    torch.cuda.synchronize()
+    want = obwd.csa_sparse_attn_bwd(dec(x["q"], fmt), q_pos0, dec(x["k_c"], fmt), dec(x["v_c"], fmt), idx,
+                                    dec(x["k_raw"], fmt), dec(x["v_raw"], fmt), raw_pos0, W, dec(x["sink"], "f32"),
+                                    dec(x["dout"], fmt))
+    _check(fmt, g, want)
