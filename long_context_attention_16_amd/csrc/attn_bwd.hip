@@ -13,11 +13,16 @@
 //   dv_r = sum_h P_hr dO_h;  dz_h = -exp(z_h - lse_h) Dl_h.
 //
 // Design, in three parts.
-//  * Query pass, workgroup = (query row, group of 4 heads): the query's
-//    source rows go through LDS in tiles of 8 (f32, window keys rotated in
-//    LDS), logits and dP by 4 threads per dot product, dq accumulated in
-//    registers. It writes, for every (query, source slot, head), P and
-//    dS / sqrt(D), and the rotated q, for the second part.
+//  * Query pass: bf16 with D = 128 on MFMA, workgroup = (query row, group
+//    of 16 heads), two waves; the query's source rows stream HBM -> LDS in
+//    double-buffered tiles of 32 (the forward's tiles); S^T = K Q^T and
+//    dP^T = V dO^T for its 16 rows of each tile per wave, P = exp(l - lse)
+//    and dS, the pair swaps dS (bf16) through LDS and each wave adds
+//    dq^T += K^T dS^T for its half of D (K read with the LDS transpose).
+//    Other shapes: workgroup = (query row, group of 4 heads), tiles of 8 rows
+//    in LDS as f32, dot products on the vector units. Either writes, for
+//    every (query, source slot, head), P and dS / sqrt(D), and the rotated
+//    q, for the second part.
 //  * Inverse index (CSA): the (query, slot) pairs that select each
 //    compressed entry, grouped by entry (counts, a scan, a fill). HCA entries
 //    and window rows need none: the queries that use them form a range.
@@ -31,6 +36,7 @@
 // The sinks' per-query parts are summed in query order.
 #include "common.hpp"
 #include "launch.hpp"
+#include "attn_tile.hpp"
 
 namespace csa {
 
@@ -297,6 +303,196 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) 
   if (tid < HG && h0 + tid < p.H) {
     const int h = h0 + tid;
     g.w.dsink_part[qrow * p.H + h] = p.sink ? -__expf(p.sink[h] - s_lse[tid]) * s_dl[tid] : 0.f;
+  }
+}
+
+// Query pass on MFMA (bf16, D = 128): see the header comment. Wave w of the
+// pair computes S and dP for rows 16w..16w+15 of each 32-row tile (lane
+// (g, l16): head l16, rows 4g..4g+3 of those), and accumulates dq for dims
+// w*D/2 .. w*D/2 + D/2 - 1 over all 32 rows.
+template <int D, bool HCA>
+__global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs g) {
+  using T = uint16_t;
+  const AttnArgs& p = g.a;
+  constexpr int NW = 2, NT = NW * kWave;
+  constexpr int ROWB = D * 2;
+  constexpr int NL = 32 * ROWB / 1024;  // LDS lines per tile
+  constexpr int LOADS = 2 * NL / NW;    // copies per wave per tile
+  constexpr int QN = D / 32;            // k-steps of 32 dims
+  constexpr int CAP = 2048;             // idx slots staged (topk <= 2048)
+  static_assert(D == 128, "double-buffered tiles of 32 rows of 256 bytes");
+  __shared__ __attribute__((aligned(16))) uint8_t Ks0[NL * k_line<T, D>()];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
+  __shared__ __attribute__((aligned(16))) uint8_t Ks1[NL * k_line<T, D>()];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs1[NL * kLineB];
+  __shared__ float rc[32][kRopePairs + 1], rs_[32][kRopePairs + 1];  // one tile's (barriers between uses)
+  __shared__ int kind[2][32];
+  __shared__ int64_t rpos[2][32];
+  __shared__ float qcos[kRopePairs], qsin[kRopePairs];
+  __shared__ int sidx[HCA ? 1 : CAP];
+  __shared__ uint2 xch[NW][kWave];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int gq = lane / 16, l16 = lane % 16;
+  const int ngroups = (p.H + 15) / 16;
+  const int64_t qrow = blockIdx.x / ngroups;
+  const int h = (int)(blockIdx.x % ngroups) * 16 + l16;
+  const bool hok = h < p.H;
+  SplitInfo si;
+  si.b = (int)(qrow / p.Lq);
+  si.t = p.q_pos0 + qrow % p.Lq;
+  si.n_c = HCA ? (int)((si.t + 1) / p.m) : p.topk;
+  si.lo = si.t - p.W + 1 > 0 ? si.t - p.W + 1 : 0;
+  si.row_lo = attn_raw_row(p, si.lo);
+  si.n_w = p.W > 0 ? (int)(si.t - si.lo + 1) : 0;
+  const int S = si.n_c + p.W;
+  si.s0 = 0;
+  si.s1 = S;
+  const int ntiles = (S + 31) / 32;
+
+  if constexpr (!HCA)
+    for (int r = tid; r < si.n_c; r += NT) sidx[r] = p.idx[qrow * p.topk + r];
+  const double rev = kRopeRev[tid % kRopePairs];
+  if (tid < kRopePairs) rope_cos_sin_f(si.t, rev, &qcos[tid], &qsin[tid]);
+  __syncthreads();
+  // q, dO and out fragments (B operands: head l16, dims 32s + 8g ..), issued
+  // before the tile copies so that waiting for them leaves the copies in flight
+  const int64_t hrow = (qrow * p.H + (hok ? h : 0)) * D;
+  uint4 qraw[QN], draw[QN], oraw[QN];
+#pragma unroll
+  for (int s = 0; s < QN; ++s) {
+    qraw[s] = *reinterpret_cast<const uint4*>((const T*)p.q + hrow + 32 * s + 8 * gq);
+    draw[s] = *reinterpret_cast<const uint4*>((const T*)g.dout + hrow + 32 * s + 8 * gq);
+    oraw[s] = *reinterpret_cast<const uint4*>((const T*)p.out + hrow + 32 * s + 8 * gq);
+  }
+  const float lse = hok ? p.lse[qrow * p.H + h] : 0.f;
+  issue_tile<T, D, NW, HCA, CAP>(p, si, sidx, 0, Ks0, Vs0, kind[0], rpos[0]);
+  issue_tile<T, D, NW, HCA, CAP>(p, si, sidx, 32, Ks1, Vs1, kind[1], rpos[1]);
+  bf16x8 qf[QN], dof[QN];
+  float dl = 0.f;
+#pragma unroll
+  for (int s = 0; s < QN; ++s) {
+    const int d0 = 32 * s + 8 * gq;
+    uint4 raw = hok ? qraw[s] : make_uint4(0, 0, 0, 0);
+    if (d0 >= D - kRopeDims) {
+      float v[8];
+      Chunk<T>::unpack(raw, v);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int pr = (d0 + e - (D - kRopeDims)) / 2;
+        const float c = qcos[pr], sn = qsin[pr], x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * c - x1 * sn;
+        v[e + 1] = x0 * sn + x1 * c;
+      }
+      raw = Chunk<T>::pack(v);
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+    const uint4 dr = hok ? draw[s] : make_uint4(0, 0, 0, 0);
+    dof[s] = __builtin_bit_cast(bf16x8, dr);
+    float dv[8], ov[8];
+    Chunk<T>::unpack(dr, dv);
+    Chunk<T>::unpack(oraw[s], ov);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dl = fmaf(dv[e], ov[e], dl);
+    // the rotated q (bf16, as attended) for the key/value pass
+    if (wave == 0 && hok) *reinterpret_cast<uint4*>((T*)g.w.qr + hrow + d0) = raw;
+  }
+  dl += __shfl_xor(dl, 16, kWave);
+  dl += __shfl_xor(dl, 32, kWave);
+  if (wave == 0 && gq == 0 && hok)
+    g.w.dsink_part[qrow * p.H + h] = p.sink ? -__expf(p.sink[h] - lse) * dl : 0.f;
+  const float lse2 = hok ? lse * kLog2e : INFINITY;  // padded heads: P = 0
+  const float cscale = kLog2e / sqrtf((float)D);
+  const float rsq = 1.f / sqrtf((float)D);
+  f32x4 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float2* pdq = g.w.pds + qrow * (int64_t)g.S * p.H + h;
+  attn_lds_barrier();  // row kinds/positions of the first tiles are visible
+
+  auto step = [&](int tt, uint8_t* Kb, uint8_t* Vb, int bi) {
+    const int ts = 32 * tt;
+    const bool win = si.n_w > 0 && ts + 32 > si.n_c;
+    if (win) rope_table(kind[bi], rpos[bi], rc, rs_, NT, rev);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));  // this tile's copies (the next tile's may fly)
+    attn_lds_barrier();
+    if (win) {
+      rope_rows_lds<T, D>(Kb, kind[bi], rc, rs_, NT);
+      attn_lds_barrier();
+    }
+    // S^T and dP^T for this wave's 16 rows
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 kf[QN], vf[QN];
+#pragma unroll
+    for (int s = 0; s < QN; ++s) {
+      kf[s] = *reinterpret_cast<const uint4*>(Kb + lds_pos<ROWB, k_line<T, D>()>(16 * wave + l16, (32 * s + 8 * gq) * 2));
+      vf[s] = *reinterpret_cast<const uint4*>(Vb + lds_pos<ROWB, kLineB>(16 * wave + l16, (32 * s + 8 * gq) * 2));
+    }
+#pragma unroll
+    for (int s = 0; s < QN; ++s) {
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], sacc, 0, 0, 0);
+      pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[s]), dof[s], pacc, 0, 0, 0);
+    }
+    float ds[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * wave + 4 * gq + v, sp = ts + row;
+      const bool ok = hok && kind[bi][row] != 0;
+      const float pv = ok ? exp2f(sacc[v] * cscale - lse2) : 0.f;
+      ds[v] = pv * (pacc[v] - dl);
+      if (hok && sp < S) pdq[(int64_t)sp * p.H] = make_float2(pv, ds[v] * rsq);
+    }
+    // dS^T of all 32 rows as the B operand: rows 4g..4g+3 and 16+4g..16+4g+3
+    const uint2 mine = make_uint2((uint32_t)f32_to_bf16_bits(ds[0]) | ((uint32_t)f32_to_bf16_bits(ds[1]) << 16),
+                                  (uint32_t)f32_to_bf16_bits(ds[2]) | ((uint32_t)f32_to_bf16_bits(ds[3]) << 16));
+    xch[wave][lane] = mine;
+    attn_lds_barrier();
+    const uint2 oth = xch[wave ^ 1][lane];
+    const uint2 t0 = wave == 0 ? mine : oth, t1 = wave == 0 ? oth : mine;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(t0.x, t0.y, t1.x, t1.y));
+    // dq^T += K^T dS^T for this wave's half of D (transposed LDS reads of K)
+    const int dt0 = wave * (D / 32);
+    const int j4 = l16 / 4, jm = l16 % 4;
+    const int off_a = lds_pos<ROWB, k_line<T, D>()>(4 * gq + j4, jm * 8) + dt0 * 32;
+    int off_b = lds_pos<ROWB, k_line<T, D>()>(16 + 4 * gq + j4, jm * 8) + dt0 * 32;
+    __asm__ volatile("" : "+v"(off_b));  // keeps the reads' LDS alias information (see the forward)
+    v4i16 lo4[D / 32], hi4[D / 32];
+#pragma unroll
+    for (int q = 0; q < D / 32; ++q) {
+      lo4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Kb + off_a + q * 32));
+      hi4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Kb + off_b + q * 32));
+    }
+#pragma unroll
+    for (int q = 0; q < D / 32; ++q) {
+      const short8_t kk = {lo4[q][0], lo4[q][1], lo4[q][2], lo4[q][3], hi4[q][0], hi4[q][1], hi4[q][2], hi4[q][3]};
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk), pf, acc[q], 0, 0, 0);
+    }
+    attn_lds_barrier();
+    issue_tile<T, D, NW, HCA, CAP>(p, si, sidx, 32 * (tt + 2), Kb, Vb, kind[bi], rpos[bi]);
+  };
+  for (int tt = 0; tt < ntiles; tt += 2) {
+    step(tt, Ks0, Vs0, 0);
+    if (tt + 1 < ntiles) step(tt + 1, Ks1, Vs1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+  if (!hok) return;
+  // dq = RoPE^T(sum dS k, t) / sqrt(D): lane holds dims 16(dt0 + q) + 4g .. + 3 of head h
+  float* dqrow = g.dq + (qrow * p.H + h) * D;
+#pragma unroll
+  for (int q = 0; q < D / 32; ++q) {
+    const int d = 16 * (wave * (D / 32) + q) + 4 * gq;
+    float x[4] = {acc[q][0] * rsq, acc[q][1] * rsq, acc[q][2] * rsq, acc[q][3] * rsq};
+    if (d >= D - kRopeDims) {
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const int pr = (d + e - (D - kRopeDims)) / 2;
+        const float c = qcos[pr], sn = qsin[pr], x0 = x[e], x1 = x[e + 1];
+        x[e] = x0 * c + x1 * sn;
+        x[e + 1] = -x0 * sn + x1 * c;
+      }
+    }
+    *reinterpret_cast<float4*>(dqrow + d) = make_float4(x[0], x[1], x[2], x[3]);
   }
 }
 
@@ -617,8 +813,12 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
   else hipLaunchKernelGGL((attn_bwd_q_kernel<TT, DD, false>), grid, dim3(kBwdThreads), 0, st, g)
     if (kv_dtype == 0) {
       if (a.D == 128) { CSA_BWD(float, 128); } else { CSA_BWD(float, 512); }
+    } else if (a.D == 128) {
+      const dim3 mgrid((unsigned)(rows * ((a.H + 15) / 16)));
+      if (hca) hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, true>), mgrid, dim3(2 * kWave), 0, st, g);
+      else hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, false>), mgrid, dim3(2 * kWave), 0, st, g);
     } else {
-      if (a.D == 128) { CSA_BWD(uint16_t, 128); } else { CSA_BWD(uint16_t, 512); }
+      CSA_BWD(uint16_t, 512);
     }
 #undef CSA_BWD
   }

@@ -62,6 +62,8 @@ def _check(fmt, g, want):
     ("bf16", 2, 1, 64, 512, 512, 128, 5000, True),  # decode head layout
     ("bf16", 1, 5, 16, 128, 24, 20, 10, True),    # windows cut at position 0, few entries
     ("f32", 1, 4, 4, 128, 16, 0, 200, True),      # no window
+    ("bf16", 2, 3, 20, 128, 100, 40, 700, True),  # two 16-head groups (the second padded), tiles across the window
+    ("bf16", 1, 7, 4, 128, 64, 128, 3000, True),  # the prefill head layout
 ])
 def test_sparse_attn_bwd(fmt, B, Lq, H, D, k, W, q_pos0, sink):
     m = 4
@@ -85,6 +87,7 @@ def test_sparse_attn_bwd(fmt, B, Lq, H, D, k, W, q_pos0, sink):
 @pytest.mark.parametrize("fmt,B,Lq,H,D,m,q_pos0,W", [
     ("bf16", 1, 1, 16, 512, 128, 70000, 128),
     ("f32", 1, 6, 4, 128, 4, 250, 16),            # prefill rows with ragged n(t)
+    ("bf16", 2, 5, 4, 128, 4, 130, 24),           # bf16 D = 128: the MFMA query pass
 ])
 def test_hca_attn_bwd(fmt, B, Lq, H, D, m, q_pos0, W):
     N_cap = (q_pos0 + Lq) // m + 1
