@@ -47,7 +47,6 @@ constexpr int kBwdHeads = 4;   // heads per query-pass workgroup
 constexpr int kBwdRows = 8;    // source rows per tile
 constexpr int kKvThreads = 256;
 constexpr int kKvWaves = kKvThreads / kWave;
-constexpr int kKvList = 1024;  // pairs of an entry staged in LDS at once
 constexpr int kScanBlock = 4096;  // counts per scan block (256 threads x 16)
 constexpr float kFixScale = 4294967296.f;  // 2^32: fixed-point unit 2^-32
 
@@ -74,6 +73,8 @@ struct BwdKvArgs {
   AttnArgs a;
   int S;
   int listed;  // CSA with at least one pair: the inverse index is built
+  int64_t wr0;  // raw rows [wr0, wr0 + nwr) of each sequence are in some query's window
+  int nwr;
   const void* dout;
   BwdWs w;
   float *dk_c, *dv_c, *dk_raw, *dv_raw;
@@ -578,27 +579,73 @@ __global__ void bwd_fill_kernel(AttnArgs p, int64_t npairs, const int* off, cons
 }
 
 // ------------------------------------------------------- key/value pass
-// Workgroup = one compressed entry (blocks [0, B * N_cap)) or one raw row
-// (the rest). Wave w takes pairs w*U.. of every kKvWaves*U; lane l owns the
-// VPT consecutive dims l*VPT.. of the row.
+// Sort a[0..m) ascending in LDS (m a power of two; bitonic network, one
+// barrier per stage, every thread of the workgroup taking part).
+__device__ __forceinline__ void bitonic_sort_lds(int* a, int m) {
+  for (int k = 2; k <= m; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < m / 2; i += blockDim.x) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1)), hi = lo | j;
+        const bool up = (lo & k) == 0;
+        const int x = a[lo], y = a[hi];
+        if ((x > y) == up) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// Sort a[0..n) (distinct values, n <= 2 * blockDim.x) ascending in LDS:
+// every element's rank is the count of smaller ones (broadcast reads), one
+// barrier, then each is written at its rank.
+__device__ __forceinline__ void rank_sort_lds(int* a, int n) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int x0 = t < n ? a[t] : 0, x1 = t + nt < n ? a[t + nt] : 0;
+  int r0 = 0, r1 = 0;
+  for (int j = 0; j < n; ++j) {
+    const int y = a[j];
+    r0 += y < x0;
+    r1 += y < x1;
+  }
+  __syncthreads();
+  if (t < n) a[r0] = x0;
+  if (t + nt < n) a[r1] = x1;
+  __syncthreads();
+}
+
+// Workgroup = one compressed entry (blocks [0, B * N_cap)) or one raw row of
+// the window range (the rest; raw rows outside it are zeroed by
+// bwd_zero_rows_kernel). A lane owns 8 consecutive dims of the row; the D/8 lanes of a
+// lane group take one pair at a time, so a wave works on 64 / (D/8) pairs
+// per step and the workgroup on kKvWaves times as many, pair k going to
+// lane group k mod NP. The pairs of a window row or an HCA entry are a query
+// range in query order; a CSA entry's list (filled in no particular order)
+// is sorted in LDS first. Each lane group then sums its pairs in float32 in
+// that fixed order, and the NP partial sums are added in a fixed order: the
+// same bits on every call. A list too long for LDS is instead summed in
+// 64-bit fixed point (units of 2^-32, exact, so order-free) in chunks.
+constexpr int kKvCap = 8192;  // pairs of an entry staged and sorted in LDS
+
 template <typename T, int D, bool HCA>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(BwdKvArgs g) {
-  constexpr int VPT = D / kWave;
-  constexpr int U = VPT <= 2 ? 4 : 2;  // pairs in flight per wave
-  constexpr int HC = 4;                 // heads per inner step
+  constexpr int LPP = D / 8;           // lanes per pair
+  constexpr int GP = kWave / LPP;      // pairs per wave step
+  constexpr int NP = kKvWaves * GP;    // pairs per workgroup step
+  static_assert(NP * 2 * D * 8 <= kKvCap * 4, "partial sums fit the list buffer");
   const AttnArgs& p = g.a;
-  __shared__ int s_list[kKvList];
-  __shared__ long long s_acc[kKvWaves - 1][2][D];
+  __shared__ __attribute__((aligned(16))) int s_buf[kKvCap];  // the list, then the partial sums
 
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int gp = lane / LPP, d0 = (lane % LPP) * 8;
   const int64_t ecount = (int64_t)p.B * p.N_cap;
   const int64_t blk = blockIdx.x;
   const bool win = blk >= ecount;
-  const int b = (int)(win ? (blk - ecount) / p.T_raw : blk / p.N_cap);
-  const int64_t r = win ? (blk - ecount) % p.T_raw : blk % p.N_cap;
+  const int b = (int)(win ? (blk - ecount) / g.nwr : blk / p.N_cap);
+  const int64_t r = win ? g.wr0 + (blk - ecount) % g.nwr : blk % p.N_cap;
   const int64_t s_pos = p.raw_pos0 + r;  // window rows: absolute position
-  // The row's pairs: CSA entries from the list, else the query range [i0, i0 + n).
   int64_t n = 0, start = 0, i0 = 0;
   if (win) {
     if (p.W > 0) {
@@ -616,117 +663,165 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_kv_kernel(BwdKvArgs g) {
     start = g.w.off[blk] + g.w.bsum[blk / kScanBlock];
   }
   const bool listed = !win && !HCA;
+  const bool exact = listed && n > kKvCap;
 
-  long long ak[VPT], av[VPT];
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) ak[v] = av[v] = 0;
   const T* qr = (const T*)g.w.qr;
   const T* dout = (const T*)g.dout;
-  const int d0 = lane * VPT;
-
-  for (int64_t c0 = 0; c0 < n; c0 += kKvList) {
-    const int cn = (int)(n - c0 < kKvList ? n - c0 : kKvList);
+  // One step of lane group gp over pairs [0, cn) of the current range:
+  // pair k = kb + gp; the sums over heads of dS qr (u) and P dO (w).
+  auto pair_sums = [&](int ks, int64_t base, float* u, float* w) {
+    int64_t qrow, slot;
     if (listed) {
-      __syncthreads();  // the previous chunk's readers are done
-      for (int i = tid; i < cn; i += kKvThreads) s_list[i] = g.w.list[start + c0 + i];
-      __syncthreads();
-    }
-    for (int k = wave * U; k < cn; k += kKvWaves * U) {
-      int64_t qrow[U], slot[U];
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        ok[u] = k + u < cn;
-        const int kk = ok[u] ? k + u : k;
-        if (listed) {
-          const int pi = __builtin_amdgcn_readfirstlane(s_list[kk]);
-          qrow[u] = pi / p.topk;
-          slot[u] = pi - qrow[u] * p.topk;
-        } else {
-          const int64_t i = i0 + c0 + kk;
-          qrow[u] = (int64_t)b * p.Lq + i;
-          if (win) {
-            const int64_t t = p.q_pos0 + i;
-            const int64_t lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;
-            slot[u] = (HCA ? (t + 1) / p.m : p.topk) + (s_pos - lo);
-          } else {
-            slot[u] = r;
-          }
-        }
+      const int pi = s_buf[ks];
+      qrow = pi / p.topk;
+      slot = pi - qrow * p.topk;
+    } else {
+      const int64_t i = i0 + base + ks;
+      qrow = (int64_t)b * p.Lq + i;
+      if (win) {
+        const int64_t t = p.q_pos0 + i;
+        const int64_t lo = t - p.W + 1 > 0 ? t - p.W + 1 : 0;
+        slot = (HCA ? (t + 1) / p.m : p.topk) + (s_pos - lo);
+      } else {
+        slot = r;
       }
-      float uk[U][VPT], uv[U][VPT];
+    }
+    const float2* pd = g.w.pds + (qrow * g.S + slot) * p.H;
+    const T* qh = qr + qrow * p.H * D + d0;
+    const T* oh = dout + qrow * p.H * D + d0;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+    for (int v = 0; v < 8; ++v) u[v] = w[v] = 0.f;
+    auto head = [&](int h, float2 w2) {
+      float xq[8], xo[8];
+      ld_vec<T, 8>(qh + h * D, xq);
+      ld_vec<T, 8>(oh + h * D, xo);
 #pragma unroll
-        for (int v = 0; v < VPT; ++v) uk[u][v] = uv[u][v] = 0.f;
-      for (int h0 = 0; h0 < p.H; h0 += HC) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float2* pd = g.w.pds + (qrow[u] * g.S + slot[u]) * p.H;
-#pragma unroll
-          for (int hh = 0; hh < HC; ++hh) {
-            const int h = h0 + hh;
-            if (h < p.H) {
-              const float2 w2 = pd[h];
-              float xq[VPT], xo[VPT];
-              ld_vec<T, VPT>(qr + (qrow[u] * p.H + h) * D + d0, xq);
-              ld_vec<T, VPT>(dout + (qrow[u] * p.H + h) * D + d0, xo);
-#pragma unroll
-              for (int v = 0; v < VPT; ++v) {
-                uk[u][v] = fmaf(w2.y, xq[v], uk[u][v]);
-                uv[u][v] = fmaf(w2.x, xo[v], uv[u][v]);
-              }
-            }
-          }
-        }
+      for (int v = 0; v < 8; ++v) {
+        u[v] = fmaf(w2.y, xq[v], u[v]);
+        w[v] = fmaf(w2.x, xo[v], w[v]);
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (ok[u])
-#pragma unroll
-          for (int v = 0; v < VPT; ++v) {
-            ak[v] += to_fix(uk[u][v]);
-            av[v] += to_fix(uv[u][v]);
-          }
+    };
+    if (p.H % 2 == 0) {  // two heads' (P, dS) per 16-byte load
+#pragma unroll 2
+      for (int h = 0; h < p.H; h += 2) {
+        const float4 w4 = *reinterpret_cast<const float4*>(pd + h);
+        head(h, make_float2(w4.x, w4.y));
+        head(h + 1, make_float2(w4.z, w4.w));
+      }
+    } else {
+      for (int h = 0; h < p.H; ++h) head(h, pd[h]);
     }
-  }
-
-  // the waves' sums (exact integers, any order), converted and written by wave 0
-  if (wave > 0)
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      s_acc[wave - 1][0][d0 + v] = ak[v];
-      s_acc[wave - 1][1][d0 + v] = av[v];
-    }
-  __syncthreads();
-  if (wave != 0) return;
-  float fk[VPT], fv[VPT];
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-#pragma unroll
-    for (int w = 0; w < kKvWaves - 1; ++w) {
-      ak[v] += s_acc[w][0][d0 + v];
-      av[v] += s_acc[w][1][d0 + v];
-    }
-    fk[v] = (float)((double)ak[v] * (1.0 / 4294967296.0));
-    fv[v] = (float)((double)av[v] * (1.0 / 4294967296.0));
-  }
-  if (win && d0 >= D - kRopeDims) {  // window keys: back to the unrotated frame
-#pragma unroll
-    for (int v = 0; v < VPT; v += 2) {
+  };
+  const int part = wave * GP + gp;
+  // The NP partial sums, added in index order; a thread finishes dims 2e,
+  // 2e+1 of dk (e < D/2) or dv (e >= D/2) and writes them.
+  auto finish = [&](float x0, float x1, int kv, int d) {
+    if (win && kv == 0 && d >= D - kRopeDims) {  // window keys: back to the unrotated frame
       float c, sn;
-      rope_cos_sin(s_pos, (d0 + v - (D - kRopeDims)) / 2, &c, &sn);
-      const float x0 = fk[v], x1 = fk[v + 1];
-      fk[v] = x0 * c + x1 * sn;
-      fk[v + 1] = -x0 * sn + x1 * c;
+      rope_cos_sin(s_pos, (d - (D - kRopeDims)) / 2, &c, &sn);
+      const float y0 = x0 * c + x1 * sn, y1 = -x0 * sn + x1 * c;
+      x0 = y0;
+      x1 = y1;
+    }
+    float* o = (kv == 0 ? (win ? g.dk_raw : g.dk_c) : (win ? g.dv_raw : g.dv_c)) +
+               (win ? (int64_t)b * p.T_raw + r : (int64_t)b * p.N_cap + r) * D;
+    *reinterpret_cast<float2*>(o + d) = make_float2(x0, x1);
+  };
+
+  if (!exact) {
+    if (listed && n > 0) {
+      if (n <= 2 * kKvThreads) {
+        for (int i = tid; i < n; i += kKvThreads) s_buf[i] = g.w.list[start + i];
+        __syncthreads();
+        rank_sort_lds(s_buf, (int)n);
+      } else {
+        const int m = 1 << (32 - __clz((int)n - 1));
+        for (int i = tid; i < m; i += kKvThreads) s_buf[i] = i < n ? g.w.list[start + i] : 0x7FFFFFFF;
+        __syncthreads();
+        bitonic_sort_lds(s_buf, m);
+      }
+    }
+    float fk[8], fv[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) fk[v] = fv[v] = 0.f;
+    for (int kb = wave * GP; kb < n; kb += NP) {
+      const int kk = kb + gp;
+      float u[8], w[8];
+      pair_sums(kk < n ? kk : kb, 0, u, w);
+      if (kk < n)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          fk[v] += u[v];
+          fv[v] += w[v];
+        }
+    }
+    __syncthreads();  // the list's readers are done
+    float* sf = reinterpret_cast<float*>(s_buf);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      sf[(part * 2 + 0) * D + d0 + v] = fk[v];
+      sf[(part * 2 + 1) * D + d0 + v] = fv[v];
+    }
+    __syncthreads();
+    for (int e = tid; e < D; e += kKvThreads) {
+      const int kv = e / (D / 2), d = 2 * (e % (D / 2));
+      float x0 = 0.f, x1 = 0.f;
+      for (int q = 0; q < NP; ++q) {
+        x0 += sf[(q * 2 + kv) * D + d];
+        x1 += sf[(q * 2 + kv) * D + d + 1];
+      }
+      finish(x0, x1, kv, d);
+    }
+  } else {
+    long long ak[8], av[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) ak[v] = av[v] = 0;
+    for (int64_t c0 = 0; c0 < n; c0 += kKvCap) {
+      const int cn = (int)(n - c0 < kKvCap ? n - c0 : kKvCap);
+      __syncthreads();  // the previous chunk's readers are done
+      for (int i = tid; i < cn; i += kKvThreads) s_buf[i] = g.w.list[start + c0 + i];
+      __syncthreads();
+      for (int kb = wave * GP; kb < cn; kb += NP) {
+        const int kk = kb + gp;
+        float u[8], w[8];
+        pair_sums(kk < cn ? kk : kb, c0, u, w);
+        if (kk < cn)
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            ak[v] += to_fix(u[v]);
+            av[v] += to_fix(w[v]);
+          }
+      }
+    }
+    __syncthreads();
+    long long* sl = reinterpret_cast<long long*>(s_buf);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      sl[(part * 2 + 0) * D + d0 + v] = ak[v];
+      sl[(part * 2 + 1) * D + d0 + v] = av[v];
+    }
+    __syncthreads();
+    for (int e = tid; e < D; e += kKvThreads) {
+      const int kv = e / (D / 2), d = 2 * (e % (D / 2));
+      long long s0 = 0, s1 = 0;
+      for (int q = 0; q < NP; ++q) {
+        s0 += sl[(q * 2 + kv) * D + d];
+        s1 += sl[(q * 2 + kv) * D + d + 1];
+      }
+      finish((float)((double)s0 * (1.0 / 4294967296.0)), (float)((double)s1 * (1.0 / 4294967296.0)), kv, d);
     }
   }
-  float* ok_ = win ? g.dk_raw + ((int64_t)b * p.T_raw + r) * D : g.dk_c + ((int64_t)b * p.N_cap + r) * D;
-  float* ov_ = win ? g.dv_raw + ((int64_t)b * p.T_raw + r) * D : g.dv_c + ((int64_t)b * p.N_cap + r) * D;
-#pragma unroll
-  for (int v = 0; v < VPT; v += 2) {
-    *reinterpret_cast<float2*>(ok_ + d0 + v) = make_float2(fk[v], fk[v + 1]);
-    *reinterpret_cast<float2*>(ov_ + d0 + v) = make_float2(fv[v], fv[v + 1]);
+}
+
+// Raw rows of no query's window: zero gradients.
+__global__ void bwd_zero_rows_kernel(float* dk, float* dv, int B, int T_raw, int D, int64_t wr0, int nwr) {
+  const int64_t n = (int64_t)B * T_raw * D;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = (i / D) % T_raw;
+    if (r < wr0 || r >= wr0 + nwr) {
+      dk[i] = 0.f;
+      dv[i] = 0.f;
+    }
   }
 }
 
@@ -822,12 +917,23 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     }
 #undef CSA_BWD
   }
-  const int64_t kv_blocks = E + (int64_t)a.B * a.T_raw;
+  // raw rows in some query's window: positions max(0, q_pos0 - W + 1) .. q_pos0 + Lq - 1
+  const int64_t lo_first = a.q_pos0 - a.W + 1 > 0 ? a.q_pos0 - a.W + 1 : 0;
+  const int64_t wr0 = a.W > 0 && a.Lq > 0 ? lo_first - a.raw_pos0 : 0;
+  const int nwr = a.W > 0 && a.Lq > 0 ? (int)(a.q_pos0 + a.Lq - lo_first) : 0;
+  if ((int64_t)a.B * a.T_raw > 0 && nwr < a.T_raw) {
+    const int64_t nz = (int64_t)a.B * a.T_raw * a.D;
+    const int zb = (int)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096);
+    hipLaunchKernelGGL(bwd_zero_rows_kernel, dim3(zb), dim3(256), 0, st, dk_raw, dv_raw, a.B, a.T_raw, a.D, wr0, nwr);
+  }
+  const int64_t kv_blocks = E + (int64_t)a.B * nwr;
   if (kv_blocks > 0) {
     BwdKvArgs g;
     g.a = a;
     g.S = S;
     g.listed = !hca && npairs > 0;
+    g.wr0 = wr0;
+    g.nwr = nwr;
     g.dout = dout;
     g.w = w;
     g.dk_c = dk_c; g.dv_c = dv_c; g.dk_raw = dk_raw; g.dv_raw = dv_raw;
