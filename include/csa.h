@@ -372,11 +372,14 @@ int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int
  *   dsink_h = -sum over queries of exp(z_h - lse_h) Dl_h.
  * A row used by several queries (an entry selected by many queries of a
  * sequence, a raw row in many windows) receives the sum of their
- * contributions. One workgroup owns each row and adds every contribution
- * (each one a sum over heads in float32) as a 64-bit integer in units of
- * 2^-32 (exact, so the result does not depend on the order; contributions
- * are clamped to |x| <= 2^30), then rounds once to float32: no atomics on
- * the gradients, the same bits on every call.
+ * contributions (each one a sum over heads in float32). One workgroup owns
+ * each row and adds them in a fixed order: query order for window rows and
+ * HCA entries; for a CSA entry its (query, slot) pairs sorted by query row
+ * and slot. An entry selected by more than 8192 (query, slot) pairs is
+ * summed instead as 64-bit integers in units of 2^-32 (exact, so
+ * order-free; contributions clamped to |x| <= 2^30) and rounded once to
+ * float32. No atomics touch the gradients: the same bits on every call, and
+ * a sequence's gradients do not depend on the rest of the batch.
  *
  * Arguments of the forward call (uniform positions, linear raw rows), plus:
  *   out, lse    the forward's outputs ([B, Lq, H, D] in kv_dtype, [B, Lq, H] f32)

@@ -28,11 +28,11 @@
 //    and window rows need none: the queries that use them form a range.
 //  * Key/value pass, workgroup = one compressed entry or one raw row: it
 //    walks the row's pairs and sums dk = sum dS RoPE(q) / sqrt(D) and
-//    dv = sum P dO over them, each pair's value (over heads, in f32) added
-//    to a 64-bit fixed-point accumulator (units of 2^-32) held in
-//    registers. Integer sums are exact, so the result is the same bits in
-//    whatever order the pairs are listed: deterministic with no atomics on
-//    the gradients and no ordering pass. Window rows are rotated back.
+//    dv = sum P dO over them in float32 in a fixed order (query order;
+//    a CSA entry's list, filled in no particular order, is sorted in LDS
+//    first), or, for lists too long for LDS, in 64-bit fixed point (units of
+//    2^-32, exact and order-free). Deterministic with no atomics on the
+//    gradients. Window rows are rotated back.
 // The sinks' per-query parts are summed in query order.
 #include "common.hpp"
 #include "launch.hpp"

@@ -155,3 +155,33 @@ def test_sparse_attn_bwd_hot_entry_and_duplicates():
                                     dec(x["k_raw"], fmt), dec(x["v_raw"], fmt), raw_pos0, W, dec(x["sink"], "f32"),
                                     dec(x["dout"], fmt))
     _check(fmt, g, want)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_sparse_attn_bwd_list_beyond_lds(fmt):
+    """Entry 3 listed in 30 slots of each of 300 queries: 9000 (query, slot)
+    pairs, more than the key/value pass sorts in LDS, so that entry is summed
+    in 64-bit fixed point; the other entries in float32 in sorted order."""
+    B, Lq, H, D, k, W, q_pos0, m = 1, 300, 4, 128, 40, 16, 100, 4
+    N_cap = (q_pos0 + Lq) // m + 1
+    raw_pos0 = q_pos0 - W
+    T_raw = q_pos0 + Lq - raw_pos0
+    x = _inputs(fmt, B, Lq, H, D, N_cap, T_raw, seed=21)
+    rng = np.random.default_rng(4)
+    idx = np.full((B, Lq, k), 3, dtype=np.int32)
+    for i in range(Lq):
+        n = (q_pos0 + i + 1) // m
+        idx[0, i, 30:] = rng.choice(np.arange(4, n), size=k - 30, replace=False)
+    it = torch.from_numpy(idx).to(DEV)
+    out, lse = csa.sparse_attn(x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0)
+    args = (x["q"], x["k_c"], x["v_c"], it, x["k_raw"], x["v_raw"], raw_pos0, W, x["sink"], q_pos0, out, lse,
+            x["dout"])
+    g = csa.sparse_attn_bwd(*args)
+    g2 = csa.sparse_attn_bwd(*args)
+    torch.cuda.synchronize()
+    want = obwd.csa_sparse_attn_bwd(dec(x["q"], fmt), q_pos0, dec(x["k_c"], fmt), dec(x["v_c"], fmt), idx,
+                                    dec(x["k_raw"], fmt), dec(x["v_raw"], fmt), raw_pos0, W, dec(x["sink"], "f32"),
+                                    dec(x["dout"], fmt))
+    _check(fmt, g, want)
+    for a, b in zip(g, g2):
+        assert torch.equal(a, b)
