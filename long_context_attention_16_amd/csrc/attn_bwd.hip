@@ -63,6 +63,7 @@ struct BwdWs {
 
 struct AttnBwdArgs {
   AttnArgs a;
+  int* cnt;  // CSA: selections of each compressed entry, counted by head group 0 (else nullptr)
   int S;  // source slots per query row (pds stride): topk + W (CSA), n(t_last) + W (HCA)
   const void* dout;
   float* dq;
@@ -172,6 +173,11 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) 
   const int n_w = p.W > 0 ? (int)(t - lo + 1) : 0;
   const int S = n_c + p.W;
   const float rs = 1.f / sqrtf((float)D);
+  if (!HCA && g.cnt && h0 == 0)
+    for (int r = tid; r < n_c; r += NT) {
+      const int32_t j = p.idx[qrow * p.topk + r];
+      if (j >= 0 && j < p.N_cap) atomicAdd(g.cnt + (int64_t)b * p.N_cap + j, 1);
+    }
 
   // q (rotated at t), dO, and Dl_h = <dO_h, o_h> for the group's heads
   const T* qb = (const T*)p.q + (qrow * p.H) * D;
@@ -352,8 +358,14 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
   si.s1 = S;
   const int ntiles = (S + 31) / 32;
 
-  if constexpr (!HCA)
-    for (int r = tid; r < si.n_c; r += NT) sidx[r] = p.idx[qrow * p.topk + r];
+  if constexpr (!HCA) {
+    const bool count = g.cnt && blockIdx.x % ngroups == 0;
+    for (int r = tid; r < si.n_c; r += NT) {
+      const int32_t j = p.idx[qrow * p.topk + r];
+      sidx[r] = j;
+      if (count && j >= 0 && j < p.N_cap) atomicAdd(g.cnt + (int64_t)si.b * p.N_cap + j, 1);
+    }
+  }
   const double rev = kRopeRev[tid % kRopePairs];
   if (tid < kRopePairs) rope_cos_sin_f(si.t, rev, &qcos[tid], &qsin[tid]);
   __syncthreads();
@@ -502,21 +514,6 @@ __global__ void bwd_zero_kernel(int* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
-// Entry of flat pair pi (= qrow * topk + slot), or -1 when the slot is masked.
-__device__ __forceinline__ int64_t pair_entry(const AttnArgs& p, int64_t pi) {
-  const int32_t j = p.idx[pi];
-  if (j < 0 || j >= p.N_cap) return -1;
-  const int64_t b = pi / p.topk / p.Lq;
-  return b * p.N_cap + j;
-}
-
-__global__ void bwd_count_kernel(AttnArgs p, int64_t npairs, int* cnt) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = pair_entry(p, i);
-    if (e >= 0) atomicAdd(cnt + e, 1);
-  }
-}
-
 // Exclusive scan of 256 per-thread values in LDS (Hillis-Steele); returns
 // this thread's exclusive prefix and *total.
 __device__ __forceinline__ int scan256(int v, int* buf, int* total) {
@@ -571,10 +568,13 @@ __global__ __launch_bounds__(256) void bwd_scan_top_kernel(int* bsum, int n) {
   }
 }
 
-__global__ void bwd_fill_kernel(AttnArgs p, int64_t npairs, const int* off, const int* bsum, int* cur, int* list) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = pair_entry(p, i);
-    if (e >= 0) list[off[e] + bsum[e / kScanBlock] + atomicAdd(cur + e, 1)] = (int)i;
+// Each valid pair i (= qrow * topk + slot, < 2^31) into its entry's list.
+__global__ void bwd_fill_kernel(AttnArgs p, int npairs, const int* off, const int* bsum, int* cur, int* list) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += gridDim.x * blockDim.x) {
+    const int32_t j = p.idx[i];
+    if (j < 0 || j >= p.N_cap) continue;
+    const int64_t e = (int64_t)(i / p.topk / p.Lq) * p.N_cap + j;
+    list[off[e] + bsum[e / kScanBlock] + atomicAdd(cur + e, 1)] = i;
   }
 }
 
@@ -883,21 +883,16 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
   const int64_t rows = (int64_t)a.B * a.Lq;
   const int64_t E = (int64_t)a.B * a.N_cap;
   const int64_t npairs = rows * a.topk;
-  // inverse index of the selections (CSA)
-  if (!hca && npairs > 0) {
+  const bool listed = !hca && npairs > 0;
+  if (listed) {  // counters of the inverse index, counted by the query pass
     const int64_t nz = (int64_t)(2 * z.cnt / sizeof(int));
     const int zb = (int)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096);
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(zb), dim3(256), 0, st, w.cnt, nz);
-    const int pb = (int)((npairs + 255) / 256 < 4096 ? (npairs + 255) / 256 : 4096);
-    hipLaunchKernelGGL(bwd_count_kernel, dim3(pb), dim3(256), 0, st, a, npairs, w.cnt);
-    const int nblk = (int)((E + kScanBlock - 1) / kScanBlock);
-    hipLaunchKernelGGL(bwd_scan_block_kernel, dim3(nblk), dim3(256), 0, st, w.cnt, E, w.off, w.bsum);
-    hipLaunchKernelGGL(bwd_scan_top_kernel, dim3(1), dim3(256), 0, st, w.bsum, nblk);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(pb), dim3(256), 0, st, a, npairs, w.off, w.bsum, w.cur, w.list);
   }
   if (rows > 0) {
     AttnBwdArgs g;
     g.a = a;
+    g.cnt = listed ? w.cnt : nullptr;
     g.S = S;
     g.dout = dout;
     g.dq = dq;
@@ -917,6 +912,13 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     }
 #undef CSA_BWD
   }
+  if (listed) {  // offsets (scan of the counts), then the lists
+    const int nblk = (int)((E + kScanBlock - 1) / kScanBlock);
+    hipLaunchKernelGGL(bwd_scan_block_kernel, dim3(nblk), dim3(256), 0, st, w.cnt, E, w.off, w.bsum);
+    hipLaunchKernelGGL(bwd_scan_top_kernel, dim3(1), dim3(256), 0, st, w.bsum, nblk);
+    const int pb = (int)((npairs + 255) / 256 < 4096 ? (npairs + 255) / 256 : 4096);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(pb), dim3(256), 0, st, a, (int)npairs, w.off, w.bsum, w.cur, w.list);
+  }
   // raw rows in some query's window: positions max(0, q_pos0 - W + 1) .. q_pos0 + Lq - 1
   const int64_t lo_first = a.q_pos0 - a.W + 1 > 0 ? a.q_pos0 - a.W + 1 : 0;
   const int64_t wr0 = a.W > 0 && a.Lq > 0 ? lo_first - a.raw_pos0 : 0;
@@ -931,7 +933,7 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     BwdKvArgs g;
     g.a = a;
     g.S = S;
-    g.listed = !hca && npairs > 0;
+    g.listed = listed;
     g.wr0 = wr0;
     g.nwr = nwr;
     g.dout = dout;
