@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) 
 // pair computes S and dP for rows 16w..16w+15 of each 32-row tile (lane
 // (g, l16): head l16, rows 4g..4g+3 of those), and accumulates dq for dims
 // w*D/2 .. w*D/2 + D/2 - 1 over all 32 rows.
-template <int D, bool HCA>
+template <int D, bool HCA, int CAP>
 __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs g) {
   using T = uint16_t;
   const AttnArgs& p = g.a;
@@ -326,13 +326,13 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
   constexpr int NL = 32 * ROWB / 1024;  // LDS lines per tile
   constexpr int LOADS = 2 * NL / NW;    // copies per wave per tile
   constexpr int QN = D / 32;            // k-steps of 32 dims
-  constexpr int CAP = 2048;             // idx slots staged (topk <= 2048)
+  // CAP: idx slots staged (topk <= CAP). LDS stays under 40 KB at CAP 1024,
+  // four workgroups per CU.
   static_assert(D == 128, "double-buffered tiles of 32 rows of 256 bytes");
   __shared__ __attribute__((aligned(16))) uint8_t Ks0[NL * k_line<T, D>()];
   __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[NL * k_line<T, D>()];
   __shared__ __attribute__((aligned(16))) uint8_t Vs1[NL * kLineB];
-  __shared__ float rc[32][kRopePairs + 1], rs_[32][kRopePairs + 1];  // one tile's (barriers between uses)
   __shared__ int kind[2][32];
   __shared__ int64_t rpos[2][32];
   __shared__ float qcos[kRopePairs], qsin[kRopePairs];
@@ -427,11 +427,19 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
   auto step = [&](int tt, uint8_t* Kb, uint8_t* Vb, int bi) {
     const int ts = 32 * tt;
     const bool win = si.n_w > 0 && ts + 32 > si.n_c;
-    if (win) rope_table(kind[bi], rpos[bi], rc, rs_, NT, rev);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));  // this tile's copies (the next tile's may fly)
     attn_lds_barrier();
-    if (win) {
-      rope_rows_lds<T, D>(Kb, kind[bi], rc, rs_, NT);
+    if (win) {  // window keys rotated in LDS; thread t always takes pair t % 32
+      for (int e = tid; e < 32 * kRopePairs; e += NT) {
+        const int r = e / kRopePairs, pr = e % kRopePairs;
+        if (kind[bi][r] != 2) continue;
+        float c, sn;
+        rope_cos_sin_f(rpos[bi][r], rev, &c, &sn);
+        uint32_t* wp = reinterpret_cast<uint32_t*>(Kb + lds_pos<ROWB, k_line<T, D>()>(r, (D - kRopeDims + 2 * pr) * 2));
+        const uint32_t v = *wp;
+        const float x0 = bf16_bits_to_f32((uint16_t)(v & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(v >> 16));
+        *wp = (uint32_t)f32_to_bf16_bits(x0 * c - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * c) << 16);
+      }
       attn_lds_barrier();
     }
     // S^T and dP^T for this wave's 16 rows
@@ -905,8 +913,9 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
       if (a.D == 128) { CSA_BWD(float, 128); } else { CSA_BWD(float, 512); }
     } else if (a.D == 128) {
       const dim3 mgrid((unsigned)(rows * ((a.H + 15) / 16)));
-      if (hca) hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, true>), mgrid, dim3(2 * kWave), 0, st, g);
-      else hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, false>), mgrid, dim3(2 * kWave), 0, st, g);
+      if (hca) hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, true, 1>), mgrid, dim3(2 * kWave), 0, st, g);
+      else if (a.topk <= 1024) hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, false, 1024>), mgrid, dim3(2 * kWave), 0, st, g);
+      else hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<128, false, 2048>), mgrid, dim3(2 * kWave), 0, st, g);
     } else {
       CSA_BWD(uint16_t, 512);
     }
