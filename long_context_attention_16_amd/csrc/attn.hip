@@ -257,7 +257,6 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[DBUF ? NL * k_line<T, D>() : 16];
   __shared__ __attribute__((aligned(16))) uint8_t Vs1[DBUF ? NL * kLineB : 16];
-  __shared__ float rc[NBUF][32][kRopePairs + 1], rs[NBUF][32][kRopePairs + 1];
   __shared__ int kind[NBUF][32];
   __shared__ int64_t rpos[NBUF][32];
   __shared__ float qcos[kRopePairs], qsin[kRopePairs];
@@ -359,18 +358,18 @@ __global__ __launch_bounds__(NW * kWave) void attn_kernel(AttnArgs p) {
   for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float cscale = kLog2e / sqrtf((float)D);
 
-  // One tile: rope table while its loads fly, wait for them, rotate window
-  // rows in LDS, compute, then reuse the buffer for the tile two ahead.
+  // One tile: wait for its loads, rotate window rows in LDS (cos/sin
+  // evaluated in place: no table, so more workgroups fit per CU), compute,
+  // then reuse the buffer for the tile two ahead.
   auto step = [&](int tt, uint8_t* Kb, uint8_t* Vb, int bi) {
     const int ts = si.s0 + 32 * tt;
     const bool win = si.n_w > 0 && ts + 32 > si.n_c;
-    // kind/rpos of this buffer were written by issue_tile before a barrier
-    if (win) rope_table(kind[bi], rpos[bi], rc[bi], rs[bi], NT, rev);
+    // kind/rpos of this buffer were written by issue_tile before a barrier.
     // This tile's copies: everything issued after them is the next tile's.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(DBUF ? LOADS : 0));
     attn_lds_barrier();
     if (win) {
-      rope_rows_lds<T, D>(Kb, kind[bi], rc[bi], rs[bi], NT);
+      rope_rows_lds_direct<T, D>(Kb, kind[bi], rpos[bi], rev, NT);
       attn_lds_barrier();
     }
     if constexpr (BF)

@@ -180,6 +180,33 @@ __device__ __forceinline__ void rope_rows_lds(uint8_t* Ks, const int* kind, floa
   }
 }
 
+// Rotate, in LDS, the last 64 dims of the tile's window rows, evaluating
+// each cos/sin where it is used: thread t always takes pair t % 32, whose
+// frequency `rev` it holds (the thread count is a multiple of 32). Same
+// values as rope_table + rope_rows_lds, without the tables' LDS.
+template <typename T, int D>
+__device__ __forceinline__ void rope_rows_lds_direct(uint8_t* Ks, const int* kind, const int64_t* pos, double rev,
+                                                     int nt_threads) {
+  constexpr int ROWB = D * (int)sizeof(T);
+  for (int e = threadIdx.x; e < 32 * kRopePairs; e += nt_threads) {
+    const int r = e / kRopePairs, pr = e % kRopePairs;
+    if (kind[r] != 2) continue;
+    float c, sn;
+    rope_cos_sin_f(pos[r], rev, &c, &sn);
+    const int d = D - kRopeDims + 2 * pr;
+    if constexpr (sizeof(T) == 2) {
+      uint32_t* w = reinterpret_cast<uint32_t*>(Ks + lds_pos<ROWB, k_line<T, D>()>(r, d * 2));
+      const uint32_t v = *w;
+      const float x0 = bf16_bits_to_f32((uint16_t)(v & 0xFFFF)), x1 = bf16_bits_to_f32((uint16_t)(v >> 16));
+      *w = (uint32_t)f32_to_bf16_bits(x0 * c - x1 * sn) | ((uint32_t)f32_to_bf16_bits(x0 * sn + x1 * c) << 16);
+    } else {
+      float2* w = reinterpret_cast<float2*>(Ks + lds_pos<ROWB, k_line<T, D>()>(r, d * 4));
+      const float2 v = *w;
+      *w = make_float2(v.x * c - v.y * sn, v.x * sn + v.y * c);
+    }
+  }
+}
+
 template <typename T, int D>
 constexpr bool attn_double_buffered(int nw) {
   return 2 * (32 * D * (int)sizeof(T) / 1024) / nw <= 32 &&
