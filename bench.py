@@ -17,8 +17,9 @@ csa_decode_state (the CSA decode step with the state cache: token append and
 block compression, then indexer top-k and attention with a position per
 sequence around 128K) and indexer_bf16_scores (the literal fp8 4 x 32 indexer
 and top-1024 of a 4096-token prefill chunk at 64K with f32 and with bf16
-scores: speedup and recall) and csa_attn_bwd (the attention backward on the
-2048-token prefill and on the 4096-token chunk at 64K).
+scores: speedup and recall), csa_attn_bwd (the attention backward on the
+2048-token prefill and on the 4096-token chunk at 64K) and csa_prefill (one
+CSA layer on the 4096-token chunk at 64K: compress, index_topk, sparse_attn).
 
 Prints one JSON line. The CPU baseline times the CPU oracle (test
 infrastructure) on a bounded sample of the same workload on the host cores.
@@ -44,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="csa_decode",
                     choices=["csa_decode", "hca_decode", "pair_1m", "indexer_fp8_prefill", "compress",
-                             "csa_decode_state", "indexer_bf16_scores", "csa_attn_bwd"])
+                             "csa_decode_state", "indexer_bf16_scores", "csa_attn_bwd", "csa_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run the 1 GiB copy (calibration run for HBM byte counters)")
@@ -446,6 +447,165 @@ def bench_bf16_scores(args, torch, csa, wl, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_prefill(args, torch, csa, wl, dev):
+    """One CSA layer on a 4096-token prefill chunk at positions 61440..65535
+    of a 64K context (config-3 shapes: bf16 KV, H = 4, D = 128, 16384
+    compressed entries, literal fp8 indexer 4 x 32, top-1024, W = 128, N(0,1)
+    inputs): csa_compress folds the chunk's own 4096 tokens into entries
+    15360..16383, csa_index_topk selects, csa_sparse_attn attends. Step time:
+    HIP-graph replays of the three calls, two input sets alternating; per-call
+    times: back-to-back launches between HIP events."""
+    from dataclasses import replace
+    s = replace(wl.CFG3, exact=False)
+    chunk = slice(s.comp_pos0 - s.raw_pos0, s.comp_pos0 - s.raw_pos0 + s.T_comp)
+    xs = []
+    for sd in (wl.SEEDS["3"], 1000 + wl.SEEDS["3"]):
+        x = wl.make_inputs(s, sd, device=dev)
+        x["kraw_chunk"] = x["k_raw"][:, chunk].contiguous()
+        x["vraw_chunk"] = x["v_raw"][:, chunk].contiguous()
+        nb = csa.index_topk_ws_bytes(s.B, s.Lq, s.q_pos0, s.m, s.N_cap, s.topk)
+        x["tws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        x["idx"] = torch.empty((s.B, s.Lq, s.topk), dtype=torch.int32, device=dev)
+        nb = csa.sparse_attn_ws_bytes(s.B, s.Lq, s.H, s.D, s.topk, s.W)
+        x["aws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
+        x["out"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty((s.B, s.Lq, s.H), dtype=torch.float32, device=dev)
+        xs.append(x)
+    torch.cuda.synchronize()
+
+    calls = {
+        "compress": lambda x: csa.compress(x["kraw_chunk"], x["vraw_chunk"], x["w_gate"], s.m, s.comp_pos0,
+                                           x["k_c"], x["v_c"]),
+        "index_topk": lambda x: csa.index_topk(x["q_i"], x["w_i"], x["k_i"], s.topk, s.q_pos0, s.m, s.idx,
+                                               x["q_i_scale"], x["k_i_scale"], ws=x["tws"], out=x["idx"]),
+        "sparse_attn": lambda x: csa.sparse_attn(x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"],
+                                                 s.raw_pos0, s.W, x["sink"], s.q_pos0, ws=x["aws"], out=x["out"],
+                                                 lse=x["lse"]),
+    }
+
+    def step(k):
+        for f in calls.values():
+            f(xs[k % 2])
+
+    for k in range(max(args.warmup, 2)):
+        step(k)
+    torch.cuda.synchronize()
+    reps = max(4, min(args.steps, 20))
+    breakdown = {}
+    for name, f in calls.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(reps):
+            f(xs[k % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        breakdown[name] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
+    graphs = []
+    for k in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(k)
+        graphs.append(g)
+    for k in range(2):
+        graphs[k].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % 2].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+
+    # algorithmic bytes (every input read once, every output written once)
+    D2 = s.D * 2
+    comp_bytes = 2 * s.T_comp * D2 + s.D * 4 + 2 * (s.T_comp // s.m) * D2
+    vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
+    n_last = (s.q_pos0 + s.Lq) // s.m
+    topk_bytes = (s.B * n_last * s.d_I + s.B * s.Lq * s.H_I * (s.d_I + 4) + 2 * s.B * vis * 4
+                  + s.B * s.Lq * s.topk * 4)
+    n_w = sum(min(s.W, s.q_pos0 + i + 1) for i in range(s.Lq))
+    rows = s.B * (s.Lq * s.topk + n_w)
+    attn_bytes = rows * 2 * D2 + s.B * s.Lq * s.topk * 4 + 2 * s.B * s.Lq * s.H * D2 + s.B * s.Lq * s.H * 4
+    roof = {"bound": "hbm", "achieved": attn_bytes / (breakdown["sparse_attn"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update(traffic=None, kernel="sparse_attn (gathered rows counted per query; 35.7 MB of distinct rows, "
+                                     "so most reads hit L2 / last-level cache)", bytes_per_launch=attn_bytes)
+    roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
+    result = {
+        "metric": "CSA prefill query-tok/s (chunk 4096 @64K, compress + index_topk + sparse_attn)",
+        "value": round(s.Lq / (ms / 1000.0), 1), "unit": "query-tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) caches, queries and indexer inputs in e4m3fn; random-init gate)",
+        "config": {"workload": "csa_prefill_chunk4096_ctx64k", "query_chunk": s.Lq, "context": s.q_pos0 + s.Lq,
+                   "compressed_entries": s.N_cap, "heads": s.H, "head_dim": s.D,
+                   "indexer": "%dx%d %s" % (s.H_I, s.d_I, s.idx), "topk": s.topk, "window": s.W},
+        "roofline": roof, "breakdown_us": breakdown,
+        "call_gbs": {"compress": round(comp_bytes / (breakdown["compress"] * 1e-6) / 1e9, 1),
+                     "index_topk": round(topk_bytes / (breakdown["index_topk"] * 1e-6) / 1e9, 1),
+                     "sparse_attn": round(roof["achieved"], 1)},
+        "timing": "value/ms_per_step: HIP-graph replays of the three calls; breakdown_us: back-to-back launches "
+                  "of each call between HIP events",
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _oracle_prefill_baseline(s, xs[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _oracle_prefill_baseline(s, x, seconds):
+    """The oracle on the prefill chunk: the chunk's compression once, then
+    query by query (indexer scores over the visible entries, top-k, attention
+    over the selected rows and the window) until `seconds` of work; the
+    compression is charged in proportion to the queries done."""
+    import numpy as np
+    import torch
+    from oracle import attention as oatt, compress as ocmp, formats, indexer as oidx, topk as otopk
+
+    def bf(t_):
+        return formats.bf16_to_f64(t_.view(torch.int16).numpy().view(np.uint16))
+
+    def f8(t_):
+        return formats.e4m3fn_to_f64(t_.view(torch.uint8).numpy())
+
+    kr_all, vr_all = x["k_raw"][0].cpu(), x["v_raw"][0].cpu()
+    kch, vch = x["kraw_chunk"][0].cpu(), x["vraw_chunk"][0].cpu()
+    w_gate = x["w_gate"].cpu().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    ocmp.compress(bf(kch), bf(vch), w_gate, s.m, s.comp_pos0)
+    t_comp = time.perf_counter() - t0
+    kc_all, vc_all = x["k_c"][0].cpu(), x["v_c"][0].cpu()
+    ki_all = f8(x["k_i"][0].cpu())
+    qi_all, wi_all, q_all = x["q_i"][0].cpu(), x["w_i"][0].cpu(), x["q"][0].cpu()
+    sink = x["sink"].cpu().numpy().astype(np.float64)
+    K, V = bf(kr_all), bf(vr_all)
+    done, spent = 0, 0.0
+    while done < s.Lq and (done == 0 or spent < seconds):
+        i = done
+        t = s.q_pos0 + i
+        n = (t + 1) // s.m
+        lo = max(0, t - s.W + 1)
+        pos = np.arange(lo, t + 1)
+        t0 = time.perf_counter()
+        sc = oidx.index_scores(f8(qi_all[i]), wi_all[i].numpy().astype(np.float64), ki_all[:n])
+        sel = otopk.topk_select(sc, s.topk)
+        sel = sel[sel >= 0]
+        oatt.attend_one(bf(q_all[i]), t, bf(kc_all[sel]), bf(vc_all[sel]), K[pos - s.raw_pos0], pos,
+                        V[pos - s.raw_pos0], sink)
+        spent += time.perf_counter() - t0
+        done += 1
+    spent += t_comp * done / s.Lq
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:
+        cores = 1
+    return {"value": round(done / spent, 4), "unit": "query-tok/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d query rows of csa_prefill_chunk4096_ctx64k (plus that share of the chunk's "
+                      "compression), %.1f s of oracle work (numpy float64)" % (done, s.Lq, spent)}
+
+
 def _oracle_bf16_baseline(s, x, seconds):
     """The oracle's indexer scores and bf16-score top-k, query by query, until
     `seconds` of oracle work have run."""
@@ -738,6 +898,9 @@ def main():
         return
     if W == "csa_attn_bwd":
         bench_attn_bwd(args, torch, csa, wl, dev)
+        return
+    if W == "csa_prefill":
+        bench_prefill(args, torch, csa, wl, dev)
         return
     if W == "csa_decode":
         shapes = [("", wl.CFG2)]
