@@ -312,6 +312,9 @@ def test_sparse_attn_edges():
     ("f32", 1, 6, 4, 128, 4, 250, 16),           # prefill rows with ragged n(t)
     ("bf16", 2, 3, 64, 512, 128, 126, 20),       # n(t) = 0 or 1
     ("f32", 1, 2, 16, 512, 4, 3000, 32),         # f32 rows of 512, several splits
+    ("bf16", 1, 4, 16, 512, 4, 700, 40),         # one head group (two waves), ragged n(t), 3 splits
+    ("bf16", 2, 2, 20, 512, 8, 3000, 64),        # two head groups, the second padded
+    ("bf16", 1, 1, 48, 512, 128, 300000, 128),   # three head groups, 16 splits
 ])
 def test_hca_attn(fmt, B, Lq, H, D, m, q_pos0, W):
     N_cap = (q_pos0 + Lq) // m + 1
