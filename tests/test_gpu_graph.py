@@ -78,3 +78,45 @@ def test_hca_graph_replays():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), r
+
+
+def test_attn_bwd_graph_replays():
+    """The attention backward captured in a HIP graph (its counters and lists
+    are cleared by its own kernels, no memsets) gives the eager bits on every
+    replay, with its workspace overwritten and eager work between replays."""
+    import numpy as np
+    B, Lq, H, D, k, W, q_pos0, m = 2, 64, 4, 128, 64, 16, 500, 4
+    N_cap = (q_pos0 + Lq) // m + 1
+    raw_pos0 = q_pos0 - W
+    T_raw = q_pos0 + Lq - raw_pos0
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    r = lambda *shape: torch.randn(shape, generator=gen, device=DEV).to(torch.bfloat16)
+    q, k_c, v_c, k_raw, v_raw, dout = r(B, Lq, H, D), r(B, N_cap, D), r(B, N_cap, D), r(B, T_raw, D), \
+        r(B, T_raw, D), r(B, Lq, H, D)
+    sink = torch.randn((H,), generator=gen, device=DEV)
+    rng = np.random.default_rng(2)
+    idx = np.full((B, Lq, k), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(Lq):
+            n = (q_pos0 + i + 1) // m
+            idx[b, i] = np.sort(rng.choice(n, size=k, replace=False))
+    it = torch.from_numpy(idx).to(DEV)
+    out, lse = csa.sparse_attn(q, k_c, v_c, it, k_raw, v_raw, raw_pos0, W, sink, q_pos0)
+    nb = csa.attn_bwd_ws_bytes(B, Lq, q_pos0, 0, H, D, N_cap, k, W)
+    ws = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=DEV)
+    args = (q, k_c, v_c, it, k_raw, v_raw, raw_pos0, W, sink, q_pos0, out, lse, dout)
+    ref = [t.clone() for t in csa.sparse_attn_bwd(*args, ws=ws)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        got = csa.sparse_attn_bwd(*args, ws=ws)
+    for rep in range(3):
+        for t in got:
+            t.fill_(7.0)
+        ws.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
