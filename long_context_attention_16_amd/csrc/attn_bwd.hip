@@ -42,6 +42,14 @@ namespace csa {
 
 namespace {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte address of an LDS object (its offset in the workgroup's LDS).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 constexpr int kBwdThreads = 256;
 constexpr int kBwdHeads = 4;   // heads per query-pass workgroup
 constexpr int kBwdRows = 8;    // source rows per tile
@@ -333,11 +341,11 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
   __shared__ __attribute__((aligned(16))) uint8_t Vs0[NL * kLineB];
   __shared__ __attribute__((aligned(16))) uint8_t Ks1[NL * k_line<T, D>()];
   __shared__ __attribute__((aligned(16))) uint8_t Vs1[NL * kLineB];
-  __shared__ int kind[2][32];
+  __shared__ __attribute__((aligned(16))) int kind[2][32];  // read 16 bytes at a time
   __shared__ int64_t rpos[2][32];
   __shared__ float qcos[kRopePairs], qsin[kRopePairs];
   __shared__ int sidx[HCA ? 1 : CAP];
-  __shared__ uint2 xch[NW][kWave];
+  __shared__ __attribute__((aligned(16))) uint2 xch[NW][kWave];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
@@ -429,7 +437,11 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
     const bool win = si.n_w > 0 && ts + 32 > si.n_c;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));  // this tile's copies (the next tile's may fly)
     attn_lds_barrier();
+#ifdef NOROPE
+    if (false) {
+#else
     if (win) {  // window keys rotated in LDS; thread t always takes pair t % 32
+#endif
       for (int e = tid; e < 32 * kRopePairs; e += NT) {
         const int r = e / kRopePairs, pr = e % kRopePairs;
         if (kind[bi][r] != 2) continue;
@@ -442,14 +454,30 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
       }
       attn_lds_barrier();
     }
-    // S^T and dP^T for this wave's 16 rows
+    // This wave's tile reads and the pair's exchange are inline-asm blocks,
+    // each waiting for its own reads before it ends: the compiler's wait
+    // analysis loses these reads' LDS alias information and would otherwise
+    // drain every copy in flight (the next tile's too) before them.
+    const uint32_t kr = lds_addr(Kb) + lds_pos<ROWB, k_line<T, D>()>(16 * wave + l16, 16 * gq);
+    const uint32_t vr = lds_addr(Vb) + lds_pos<ROWB, kLineB>(16 * wave + l16, 16 * gq);
+    const uint32_t ka = lds_addr(&kind[bi][16 * wave + 4 * gq]);
+    u32x4 kf0, kf1, kf2, kf3, vf0, vf1, vf2, vf3, kd;
+    __asm__ volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b128 %1, %9 offset:64\n\t"
+        "ds_read_b128 %2, %9 offset:128\n\t"
+        "ds_read_b128 %3, %9 offset:192\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %10 offset:64\n\t"
+        "ds_read_b128 %6, %10 offset:128\n\t"
+        "ds_read_b128 %7, %10 offset:192\n\t"
+        "ds_read_b128 %8, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kf0), "=&v"(kf1), "=&v"(kf2), "=&v"(kf3), "=&v"(vf0), "=&v"(vf1), "=&v"(vf2), "=&v"(vf3), "=&v"(kd)
+        : "v"(kr), "v"(vr), "v"(ka)
+        : "memory");
+    const u32x4 kf[QN] = {kf0, kf1, kf2, kf3}, vf[QN] = {vf0, vf1, vf2, vf3};
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 kf[QN], vf[QN];
-#pragma unroll
-    for (int s = 0; s < QN; ++s) {
-      kf[s] = *reinterpret_cast<const uint4*>(Kb + lds_pos<ROWB, k_line<T, D>()>(16 * wave + l16, (32 * s + 8 * gq) * 2));
-      vf[s] = *reinterpret_cast<const uint4*>(Vb + lds_pos<ROWB, kLineB>(16 * wave + l16, (32 * s + 8 * gq) * 2));
-    }
 #pragma unroll
     for (int s = 0; s < QN; ++s) {
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[s]), qf[s], sacc, 0, 0, 0);
@@ -459,35 +487,50 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = 16 * wave + 4 * gq + v, sp = ts + row;
-      const bool ok = hok && kind[bi][row] != 0;
+      const bool ok = hok && kd[v] != 0;
       const float pv = ok ? exp2f(sacc[v] * cscale - lse2) : 0.f;
       ds[v] = pv * (pacc[v] - dl);
       if (hok && sp < S) pdq[(int64_t)sp * p.H] = make_float2(pv, ds[v] * rsq);
     }
     // dS^T of all 32 rows as the B operand: rows 4g..4g+3 and 16+4g..16+4g+3
-    const uint2 mine = make_uint2((uint32_t)f32_to_bf16_bits(ds[0]) | ((uint32_t)f32_to_bf16_bits(ds[1]) << 16),
-                                  (uint32_t)f32_to_bf16_bits(ds[2]) | ((uint32_t)f32_to_bf16_bits(ds[3]) << 16));
-    xch[wave][lane] = mine;
-    attn_lds_barrier();
-    const uint2 oth = xch[wave ^ 1][lane];
-    const uint2 t0 = wave == 0 ? mine : oth, t1 = wave == 0 ? oth : mine;
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(t0.x, t0.y, t1.x, t1.y));
+    const u32x2 mine = {(uint32_t)f32_to_bf16_bits(ds[0]) | ((uint32_t)f32_to_bf16_bits(ds[1]) << 16),
+                        (uint32_t)f32_to_bf16_bits(ds[2]) | ((uint32_t)f32_to_bf16_bits(ds[3]) << 16)};
+    u32x2 oth;
+    __asm__ volatile(
+        "ds_write_b64 %1, %2\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_barrier\n\t"
+        "ds_read_b64 %0, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(oth)
+        : "v"(lds_addr(&xch[wave][lane])), "v"(mine), "v"(lds_addr(&xch[wave ^ 1][lane]))
+        : "memory");
+    const u32x2 t0 = wave == 0 ? mine : oth, t1 = wave == 0 ? oth : mine;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{t0[0], t0[1], t1[0], t1[1]});
     // dq^T += K^T dS^T for this wave's half of D (transposed LDS reads of K)
     const int dt0 = wave * (D / 32);
     const int j4 = l16 / 4, jm = l16 % 4;
-    const int off_a = lds_pos<ROWB, k_line<T, D>()>(4 * gq + j4, jm * 8) + dt0 * 32;
-    int off_b = lds_pos<ROWB, k_line<T, D>()>(16 + 4 * gq + j4, jm * 8) + dt0 * 32;
-    __asm__ volatile("" : "+v"(off_b));  // keeps the reads' LDS alias information (see the forward)
-    v4i16 lo4[D / 32], hi4[D / 32];
+    const uint32_t ta = lds_addr(Kb) + lds_pos<ROWB, k_line<T, D>()>(4 * gq + j4, jm * 8) + dt0 * 32;
+    const uint32_t tb = lds_addr(Kb) + lds_pos<ROWB, k_line<T, D>()>(16 + 4 * gq + j4, jm * 8) + dt0 * 32;
+    u32x2 a0, a1, a2, a3, b0, b1, b2, b3;
+    __asm__ volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+        "ds_read_b64_tr_b16 %4, %9\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:32\n\t"
+        "ds_read_b64_tr_b16 %6, %9 offset:64\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+        : "v"(ta), "v"(tb)
+        : "memory");
+    const u32x2 lo[4] = {a0, a1, a2, a3}, hi[4] = {b0, b1, b2, b3};
 #pragma unroll
     for (int q = 0; q < D / 32; ++q) {
-      lo4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Kb + off_a + q * 32));
-      hi4[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(Kb + off_b + q * 32));
-    }
-#pragma unroll
-    for (int q = 0; q < D / 32; ++q) {
-      const short8_t kk = {lo4[q][0], lo4[q][1], lo4[q][2], lo4[q][3], hi4[q][0], hi4[q][1], hi4[q][2], hi4[q][3]};
-      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk), pf, acc[q], 0, 0, 0);
+      const bf16x8 kk = __builtin_bit_cast(bf16x8, u32x4{lo[q][0], lo[q][1], hi[q][0], hi[q][1]});
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, pf, acc[q], 0, 0, 0);
     }
     attn_lds_barrier();
     issue_tile<T, D, NW, HCA, CAP>(p, si, sidx, 32 * (tt + 2), Kb, Vb, kind[bi], rpos[bi]);
