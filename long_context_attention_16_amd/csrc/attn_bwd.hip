@@ -42,14 +42,6 @@ namespace csa {
 
 namespace {
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// Byte address of an LDS object (its offset in the workgroup's LDS).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 constexpr int kBwdThreads = 256;
 constexpr int kBwdHeads = 4;   // heads per query-pass workgroup
 constexpr int kBwdRows = 8;    // source rows per tile

@@ -207,6 +207,15 @@ __device__ __forceinline__ void rope_rows_lds_direct(uint8_t* Ks, const int* kin
   }
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte address of an LDS object (its offset in the workgroup's LDS), for
+// LDS reads written in inline asm.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <typename T, int D>
 constexpr bool attn_double_buffered(int nw) {
   return 2 * (32 * D * (int)sizeof(T) / 1024) / nw <= 32 &&
