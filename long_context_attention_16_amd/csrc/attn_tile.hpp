@@ -50,7 +50,7 @@ template <> struct Chunk<float> {
 // (8 rows x 4 lanes per 32 lanes) want 1056 (264 words, 8 apart).
 constexpr int kLineB = 1024 + 32;
 template <typename T, int D> constexpr int k_line() { return sizeof(T) == 2 && D == 512 ? 1024 + 16 : kLineB; }
-constexpr int kMaxSplitRows = 128;  // CSA splits: at most 96 rows (k <= 2048, W <= 1024)
+constexpr int kMaxSplitRows = 576;  // CSA splits: at most 576 rows (k <= 2048, W <= 1024: S <= 3072)
 
 // LDS offset of byte `byte` of tile row r (rows longer than a line continue
 // in the next line, after the pad).

@@ -46,12 +46,20 @@ __device__ __forceinline__ int64_t attn_window_row(const AttnArgs& p, int64_t ro
 }
 
 // Rows per split of a query with S sources: S/16 rounded up to a multiple of
-// 32, at least 96 (three 32-row tiles, so each workgroup pipelines loads with
-// compute). A function of S alone, so the split structure never depends on
-// the batch.
+// 32 (long lists: many splits per query keep every CU busy at decode sizes),
+// at least 96 (three 32-row tiles, so each workgroup pipelines loads with
+// compute); for lists of at most 4096 sources at least half the list, up to
+// 576 rows (18 tiles): a split's fixed costs (the idx lookup before its first
+// copies, the partial write, its share of the combine) then stay small next
+// to its stream. A function of S alone, so the split structure never depends
+// on the batch.
 __host__ __device__ inline int attn_split_rows(int S) {
-  int ch = (S + 15) / 16;
-  ch = ((ch + 31) / 32) * 32;
+  int ch = ((S + 15) / 16 + 31) / 32 * 32;
+  if (S <= 4096) {
+    int half = ((S + 1) / 2 + 31) / 32 * 32;
+    half = half < 576 ? half : 576;
+    ch = ch > half ? ch : half;
+  }
   return ch < 96 ? 96 : ch;
 }
 __host__ __device__ inline int attn_nsplit(int S) {
