@@ -50,8 +50,11 @@ def test_ws_queries(lib):
     # rows of at most one chunk need no candidate lists
     assert lib.csa_topk_ws_bytes(1, 4, 200, 4, 16) == 16
     assert lib.csa_index_topk_ws_bytes(1, 4, 200, 4, 64, 16) == 1024 + 16
-    # 640 sources -> 7 splits of 96 rows; partial O + (max, sum) per split and head
-    assert lib.csa_sparse_attn_ws_bytes(32, 1, 64, 512, 512, 128) == 32 * 7 * 64 * (512 + 2) * 4
+    # 640 sources -> 2 splits of 320 rows (lists of at most 4096 sources split
+    # into at least halves); partial O + (max, sum) per split and head
+    assert lib.csa_sparse_attn_ws_bytes(32, 1, 64, 512, 512, 128) == 32 * 2 * 64 * (512 + 2) * 4
+    # 8320 sources (HCA at 1M) -> S/16 rounded to 32 = 544 rows, 16 splits
+    assert lib.hca_dense_attn_ws_bytes(16, 1, 1048575, 128, 64, 512, 128) == 16 * 16 * 64 * (512 + 2) * 4
     # one split needs no partials
     assert lib.csa_sparse_attn_ws_bytes(1, 1, 4, 128, 16, 16) == 16
     assert lib.hca_dense_attn_ws_bytes(16, 1, 1048575, 128, 64, 512, 128) > 0
