@@ -395,7 +395,7 @@ int csa_index_scores_ex(int B, int Lq, const int64_t* q_pos, int64_t q_pos0, int
  *               the weight P and dS / sqrt(D) (8 bytes; slots: topk + W for
  *               CSA, n(q_pos0 + Lq - 1) + W for HCA), the rotated q, the sink
  *               parts, and for CSA the index of the (query, slot) pairs of
- *               each compressed entry (12 bytes per entry, 4 per pair).
+ *               each compressed entry (8 bytes per entry, 8 per pair).
  * Errors: CSA_ERR_SHAPE also when B * Lq * topk >= 2^31 (pairs are indexed
  * in 32 bits).
  * hca_dense_attn_bwd: the same for hca_dense_attn (block m, every visible entry).

@@ -55,7 +55,8 @@ struct BwdWs {
   float2* pds;        // [rows][S][H]: (P, dS / sqrt(D)) of each (query, source slot, head)
   void* qr;           // [rows][H][D] RoPE(q, t) in the KV dtype
   float* dsink_part;  // [rows][H]
-  int *cnt, *cur;     // [E = B * N_cap]: selections of each compressed entry; fill cursors
+  int* cnt;           // [E = B * N_cap]: selections of each compressed entry
+  int* rank;          // [rows * topk]: each pair's rank among its entry's pairs (the counting atomic's value)
   int* off;           // [E] exclusive offsets within the entry's scan block
   int* bsum;          // [ceil(E / kScanBlock)] block totals, then their exclusive offsets
   int* list;          // [rows * topk] flat pair index qrow * topk + slot, grouped by entry
@@ -64,6 +65,7 @@ struct BwdWs {
 struct AttnBwdArgs {
   AttnArgs a;
   int* cnt;  // CSA: selections of each compressed entry, counted by head group 0 (else nullptr)
+  int* rank;  // CSA: each counted pair's rank within its entry
   int S;  // source slots per query row (pds stride): topk + W (CSA), n(t_last) + W (HCA)
   const void* dout;
   float* dq;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) 
   if (!HCA && g.cnt && h0 == 0)
     for (int r = tid; r < n_c; r += NT) {
       const int32_t j = p.idx[qrow * p.topk + r];
-      if (j >= 0 && j < p.N_cap) atomicAdd(g.cnt + (int64_t)b * p.N_cap + j, 1);
+      if (j >= 0 && j < p.N_cap) g.rank[qrow * p.topk + r] = atomicAdd(g.cnt + (int64_t)b * p.N_cap + j, 1);
     }
 
   // q (rotated at t), dO, and Dl_h = <dO_h, o_h> for the group's heads
@@ -358,12 +360,22 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
   si.s1 = S;
   const int ntiles = (S + 31) / 32;
 
+  // The query's idx slots into LDS; head group 0 counts each entry's
+  // selections, keeping the ranks the counters return in registers until the
+  // end (storing them here would wait for every atomic's round trip).
+  constexpr int RK = HCA ? 1 : (CAP + NT - 1) / NT;
+  int rk[RK];
+  const bool count = !HCA && g.cnt && blockIdx.x % ngroups == 0;
   if constexpr (!HCA) {
-    const bool count = g.cnt && blockIdx.x % ngroups == 0;
-    for (int r = tid; r < si.n_c; r += NT) {
-      const int32_t j = p.idx[qrow * p.topk + r];
-      sidx[r] = j;
-      if (count && j >= 0 && j < p.N_cap) atomicAdd(g.cnt + (int64_t)si.b * p.N_cap + j, 1);
+#pragma unroll
+    for (int it = 0; it < RK; ++it) {
+      const int r = tid + it * NT;
+      rk[it] = -1;
+      if (r < si.n_c) {
+        const int32_t j = p.idx[qrow * p.topk + r];
+        sidx[r] = j;
+        if (count && j >= 0 && j < p.N_cap) rk[it] = atomicAdd(g.cnt + (int64_t)si.b * p.N_cap + j, 1);
+      }
     }
   }
   const double rev = kRopeRev[tid % kRopePairs];
@@ -532,6 +544,12 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
     if (tt + 1 < ntiles) step(tt + 1, Ks1, Vs1, 1);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+  if constexpr (!HCA) {
+    if (count)
+#pragma unroll
+      for (int it = 0; it < RK; ++it)
+        if (rk[it] >= 0) g.rank[qrow * p.topk + tid + it * NT] = rk[it];
+  }
   if (!hok) return;
   // dq = RoPE^T(sum dS k, t) / sqrt(D): lane holds dims 16(dt0 + q) + 4g .. + 3 of head h
   float* dqrow = g.dq + (qrow * p.H + h) * D;
@@ -611,13 +629,14 @@ __global__ __launch_bounds__(256) void bwd_scan_top_kernel(int* bsum, int n) {
   }
 }
 
-// Each valid pair i (= qrow * topk + slot, < 2^31) into its entry's list.
-__global__ void bwd_fill_kernel(AttnArgs p, int npairs, const int* off, const int* bsum, int* cur, int* list) {
+// Each valid pair i (= qrow * topk + slot, < 2^31) into its entry's list, at
+// its rank from the counting atomics (no atomics here).
+__global__ void bwd_fill_kernel(AttnArgs p, int npairs, const int* off, const int* bsum, const int* rank, int* list) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < npairs; i += gridDim.x * blockDim.x) {
     const int32_t j = p.idx[i];
     if (j < 0 || j >= p.N_cap) continue;
     const int64_t e = (int64_t)(i / p.topk / p.Lq) * p.N_cap + j;
-    list[off[e] + bsum[e / kScanBlock] + atomicAdd(cur + e, 1)] = i;
+    list[off[e] + bsum[e / kScanBlock] + rank[i]] = i;
   }
 }
 
@@ -887,8 +906,8 @@ __global__ __launch_bounds__(256) void dsink_sum_kernel(const float* part, int64
 inline size_t al256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct BwdSizes {
-  size_t pds, qr, sink, cnt, off, bsum, list;
-  size_t total() const { return pds + qr + sink + 2 * cnt + off + bsum + list; }
+  size_t pds, qr, sink, cnt, off, bsum, list, rank;
+  size_t total() const { return pds + qr + sink + cnt + off + bsum + list + rank; }
 };
 
 BwdSizes bwd_sizes(int B, int Lq, int H, int D, int64_t N_cap, int S, int topk) {
@@ -901,6 +920,7 @@ BwdSizes bwd_sizes(int B, int Lq, int H, int D, int64_t N_cap, int S, int topk) 
   z.off = al256(E * sizeof(int));
   z.bsum = al256((E + kScanBlock - 1) / kScanBlock * sizeof(int));
   z.list = al256(rows * (size_t)topk * sizeof(int));
+  z.rank = z.list;
   return z;
 }
 
@@ -919,16 +939,16 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
   w.qr = w8;                       w8 += z.qr;
   w.dsink_part = (float*)w8;       w8 += z.sink;
   w.cnt = (int*)w8;                w8 += z.cnt;
-  w.cur = (int*)w8;                w8 += z.cnt;
   w.off = (int*)w8;                w8 += z.off;
   w.bsum = (int*)w8;               w8 += z.bsum;
-  w.list = (int*)w8;
+  w.list = (int*)w8;               w8 += z.list;
+  w.rank = (int*)w8;
   const int64_t rows = (int64_t)a.B * a.Lq;
   const int64_t E = (int64_t)a.B * a.N_cap;
   const int64_t npairs = rows * a.topk;
   const bool listed = !hca && npairs > 0;
   if (listed) {  // counters of the inverse index, counted by the query pass
-    const int64_t nz = (int64_t)(2 * z.cnt / sizeof(int));
+    const int64_t nz = E;
     const int zb = (int)((nz + 255) / 256 < 4096 ? (nz + 255) / 256 : 4096);
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(zb), dim3(256), 0, st, w.cnt, nz);
   }
@@ -936,6 +956,7 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     AttnBwdArgs g;
     g.a = a;
     g.cnt = listed ? w.cnt : nullptr;
+    g.rank = listed ? w.rank : nullptr;
     g.S = S;
     g.dout = dout;
     g.dq = dq;
@@ -961,7 +982,7 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     hipLaunchKernelGGL(bwd_scan_block_kernel, dim3(nblk), dim3(256), 0, st, w.cnt, E, w.off, w.bsum);
     hipLaunchKernelGGL(bwd_scan_top_kernel, dim3(1), dim3(256), 0, st, w.bsum, nblk);
     const int pb = (int)((npairs + 255) / 256 < 4096 ? (npairs + 255) / 256 : 4096);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3(pb), dim3(256), 0, st, a, (int)npairs, w.off, w.bsum, w.cur, w.list);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(pb), dim3(256), 0, st, a, (int)npairs, w.off, w.bsum, w.rank, w.list);
   }
   // raw rows in some query's window: positions max(0, q_pos0 - W + 1) .. q_pos0 + Lq - 1
   const int64_t lo_first = a.q_pos0 - a.W + 1 > 0 ? a.q_pos0 - a.W + 1 : 0;
