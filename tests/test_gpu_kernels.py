@@ -226,6 +226,8 @@ def _oracle_attn(x, fmt, idx, q_pos0, raw_pos0, W, sink, hca_m=None):
     ("f32", 1, 3, 32, 512, 24, 7, True),
     ("bf16", 1, 2, 128, 128, 300, 33, True),
     ("f32", 1, 2, 8, 512, 300, 64, True),     # f32 rows of 512 split 4 ways: 128 combine threads per row
+    ("bf16", 1, 2, 4, 128, 2048, 1024, True),  # 3072 sources: six splits of 576 rows (the staged idx slots full)
+    ("f32", 1, 2, 4, 128, 1024, 128, True),    # 1152 sources: two splits of 576 rows
 ])
 def test_sparse_attn(fmt, B, Lq, H, D, k, W, sink):
     m, q_pos0 = 4, 3000
