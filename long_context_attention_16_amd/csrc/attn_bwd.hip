@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_q_kernel(AttnBwdArgs g) 
     // and s_row passed the barrier before its dq update, which reads only
     // s_ds and s_k), then K (window rows rotated at their position) and V.
     if (tid < R) {
-      int64_t row, pos;
+      int64_t row = 0, pos = 0;  // slots past the list: masked, row 0
       s_kind[tid] = r0 + tid < S ? bwd_source<HCA>(p, b, qrow, n_c, lo, n_w, r0 + tid, &row, &pos) : 0;
       s_row[tid] = row;
       s_pos[tid] = pos;

@@ -279,7 +279,6 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
   const int g = lane / 16, l16 = lane % 16;
   const int rows = gridDim.x / kNsl;  // a query's slices on one XCD, as in phase A
   const int qrow = blockIdx.x % rows, sl = blockIdx.x / rows;
-  const DecQuery dq = dec_query(p, qrow);
   const int h = wave * 16 + l16;
   const uint16_t* prow = pp + ((int64_t)qrow * H + h) * spad;
 
