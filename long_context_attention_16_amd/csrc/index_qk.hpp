@@ -260,7 +260,8 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
   // loop over lanes). Fused: an LDS store, masked lanes writing a dump row.
   // bf16 scores (sbf): rows of score_stride(N_cap, 1) entries, each lane pair
   // stored as one word by its even lane (score_word), so every lane still
-  // issues exactly one store per put.
+  // issues exactly one store per put (the 4-head layout instead pairs two
+  // query rows per store, see compute_store).
   const int esz = sbf ? 2 : 4;
   const int64_t sstride = score_stride(N_cap, sbf);
   const uint64_t sbase = FUSE ? 0 : (uint64_t)((uint8_t*)scores + ((int64_t)b * Lq + i0) * sstride * esz);
@@ -302,6 +303,7 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
     const int jrel = tile_of(i) * 32 + l32;  // entry index
     if constexpr (HI == 4) {
       // each group of 4 registers is one query's 4 heads
+      float vv[MTILES * 4];
 #pragma unroll
       for (int mt = 0; mt < MTILES; ++mt)
 #pragma unroll
@@ -311,8 +313,33 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
           v = fmaf(w4.y, relu_bits(acc[mt][a4 * 4 + 1]), v);
           v = fmaf(w4.z, relu_bits(acc[mt][a4 * 4 + 2]), v);
           v = fmaf(w4.w, relu_bits(acc[mt][a4 * 4 + 3]), v);
-          put(mt * 8 + a4 * 2 + half, jrel, jrel < lim[mt * 4 + a4], v);
+          vv[mt * 4 + a4] = v;
         }
+      if (!FUSE && sbf) {
+        // bf16 scores, two query rows per store: of rows A = (mt, a4) and
+        // B = (mt, a4 + 1), the even lane of a pair writes A's entries
+        // (2i, 2i+1) and the odd lane B's, each getting the value it lacks
+        // from its neighbour in one swap, so every lane stores and a tile
+        // takes half the stores (the kernel is bound by their issue).
+        const bool even = (lane & 1) == 0;
+        const int j0 = jrel & ~1;
+#pragma unroll
+        for (int p = 0; p < MTILES * 4; p += 2) {
+          const int mt = p / 4, a4 = p % 4 + (even ? 0 : 1);
+          const float send = even ? vv[p + 1] : vv[p];
+          const float recv = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0xB1, 0xF, 0xF, false));
+          const float lo = even ? vv[p] : recv, hi = even ? recv : vv[p + 1];
+          const uint32_t word = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+          const int qq = mt * 8 + a4 * 2 + half;
+          const int off = j0 < lim[mt * 4 + a4] ? (int)((uint32_t)qq * srow + (uint32_t)j0 * 2u) : kDrop;
+          if constexpr (!FUSE) __builtin_amdgcn_raw_buffer_store_b32(word, srsrc, off, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < MTILES * 4; ++p)
+          put((p / 4) * 8 + (p % 4) * 2 + half, jrel, jrel < lim[p], vv[p]);
+      }
     } else {
       constexpr int gpq = HI / 8;  // register groups (of 4 rows x 2 halves) per query
       float run = 0.f;
