@@ -232,7 +232,74 @@ def bench_compress(args, torch, csa, dev):
         "timing": "HIP-graph replays of back-to-back calls per case",
         "copy_ceiling_gbs": copy_ceiling(torch, dev), "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _oracle_compress_baseline(torch, dev, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _oracle_compress_baseline(torch, dev, seconds):
+    """The oracle compressor (float64) on the main case's inputs (1M tokens,
+    D = 512, m = 4, same seed), 8192 tokens at a time until `seconds` of work;
+    GB/s counts the same algorithmic bytes as the GPU figure."""
+    import numpy as np
+    from oracle import compress as ocmp, formats
+    T, D, m = 1 << 20, 512, 4
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    k_raw = torch.randn((1, T, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_raw = torch.randn((1, T, D), generator=gen, device=dev).to(torch.bfloat16)
+    w_gate = (torch.randn((D,), generator=gen, device=dev) / D ** 0.5).cpu().numpy().astype(np.float64)
+
+    def bf(t_):
+        return formats.bf16_to_f64(t_.view(torch.int16).numpy().view(np.uint16))
+
+    done, spent, step = 0, 0.0, 8192
+    while done < T and (done == 0 or spent < seconds):
+        kr, vr = bf(k_raw[0, done:done + step].cpu()), bf(v_raw[0, done:done + step].cpu())
+        t0 = time.perf_counter()
+        ocmp.compress(kr, vr, w_gate, m, done)
+        spent += time.perf_counter() - t0
+        done += step
+    nbytes = 2 * done * D * 2 + 2 * (done // m) * D * 2
+    del k_raw, v_raw
+    torch.cuda.empty_cache()
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": "%d of %d tokens of compress_seq1m_d512_m4, %.1f s of oracle work (numpy float64)"
+                      % (done, T, spent)}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(blas) if blas else 1
+    except Exception:
+        return 1
+
+
+def _oracle_prefill_indexer_baseline(s, x, seconds):
+    """The oracle's fp8 64 x 128 indexer scores, query by query of the
+    prefill chunk, until `seconds` of work."""
+    import numpy as np
+    import torch
+    from oracle import formats, indexer as oidx
+
+    def f8(t_):
+        return formats.e4m3fn_to_f64(t_.view(torch.uint8).numpy())
+
+    ki = f8(x["k_i"][0].cpu())
+    qi, wi = x["q_i"][0].cpu(), x["w_i"][0].cpu()
+    done, spent = 0, 0.0
+    while done < s.Lq and (done == 0 or spent < seconds):
+        n = (s.q_pos0 + done + 1) // s.m
+        qd, wd = f8(qi[done]), wi[done].numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        oidx.index_scores(qd, wd, ki[:n])
+        spent += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done / spent, 4), "unit": "query-tok/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": "%d of %d query rows of %s, %.1f s of oracle work (numpy float64)"
+                      % (done, s.Lq, s.name, spent)}
 
 
 def bench_state_decode(args, torch, csa, wl, dev):
@@ -1072,11 +1139,13 @@ def main():
         "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
         "copy_ceiling_gbs": copy_ceiling(torch, dev),
     }
-    if not args.no_cpu_baseline and W != "indexer_fp8_prefill":
+    if args.no_cpu_baseline:
+        result["cpu_baseline"] = None
+    elif W == "indexer_fp8_prefill":
+        result["cpu_baseline"] = _oracle_prefill_indexer_baseline(main_shape, sets[0][0], args.cpu_seconds)
+    else:
         parts = [(s, xs[0]) for (prefix, s), xs in zip(shapes, sets)]
         result["cpu_baseline"] = cpu_baseline(cfg["workload"], parts, args.cpu_seconds)
-    else:
-        result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
 
 
