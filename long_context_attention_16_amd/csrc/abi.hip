@@ -28,8 +28,16 @@ int check_window(int Lq, int64_t q_pos0, int W, int T_raw, int64_t raw_pos0, boo
 }
 
 int attn_nsplit_max_csa(int topk, int W) { return attn_nsplit(topk + W); }
+// HCA rows of one call have different source counts (n(t) grows with t, and
+// per-sequence positions vary). The longest row's split count bounds every
+// row's only while the count is monotonic in the source count, which holds
+// up to 4096 sources; beyond, rounding the split size up to whole tiles makes
+// it dip (4608 sources: 16 splits of 288 rows; 4609: 15 of 320), so the grid
+// and the partials are sized for the maximum, 16 (a split holds at least
+// S/16 rows).
 int attn_nsplit_max_hca(int64_t q_pos0, int Lq, int m, int W) {
-  return attn_nsplit((int)n_last(q_pos0, Lq, m) + W);
+  const int S = (int)n_last(q_pos0, Lq, m) + W;
+  return S > 4096 ? 16 : attn_nsplit(S);
 }
 // Split partials: O in the KV dtype, then (max, sum) in f32.
 size_t attn_ws(int B, int Lq, int H, int D, int nsplit, int kv_bytes) {

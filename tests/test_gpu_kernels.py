@@ -317,6 +317,10 @@ def test_sparse_attn_edges():
     ("bf16", 1, 4, 16, 512, 4, 700, 40),         # one head group (two waves), ragged n(t), 3 splits
     ("bf16", 2, 2, 20, 512, 8, 3000, 64),        # two head groups, the second padded
     ("bf16", 1, 1, 48, 512, 128, 300000, 128),   # three head groups, 16 splits
+    # sources 4600 .. 4609 over the chunk: 16 splits of 288 rows up to 4608,
+    # 15 of 320 at 4609 (the split count is not monotonic in the source
+    # count), so the grid must be sized for more splits than the last row's
+    ("bf16", 1, 41, 4, 128, 4, 17887, 128),
 ])
 def test_hca_attn(fmt, B, Lq, H, D, m, q_pos0, W):
     N_cap = (q_pos0 + Lq) // m + 1
