@@ -282,6 +282,26 @@ def test_hca_attn_varlen(kv, Lq, H, D, m, W, R):
     assert_close(lse.cpu().numpy(), el, 5e-3 if kv == "bf16" else 1e-5, 1e-3, what="lse")
 
 
+def test_hca_attn_varlen_split_count_dip():
+    """The bound q_pos_max = 17924 gives 4481 + 128 = 4609 sources (15 splits
+    of 320 rows); the sequence at 17920 has 4608 (16 splits of 288): the grid
+    must hold more splits than the bound's row."""
+    kv, Lq, H, D, m, W, R = "bf16", 1, 4, 128, 4, 128, 128
+    pos = [17924, 17920, 300]
+    q_pos_max = 17924
+    N_cap = (q_pos_max + Lq) // m + 1
+    x = _attn_case(kv, len(pos), Lq, H, D, N_cap, R, seed=29)
+    q_pos = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    out, lse = csa.hca_attn_varlen(x["q"], x["k_c"], x["v_c"], m, x["k_ring"], x["v_ring"], W, x["sink"],
+                                   q_pos, q_pos_max)
+    torch.cuda.synchronize()
+    eo, el = oatt.hca_dense_attn(dec(x["q"], kv), np.array(pos), m, dec(x["k_c"], kv), dec(x["v_c"], kv),
+                                 dec(x["k_ring"], kv), dec(x["v_ring"], kv), 0, W, dec(x["sink"], "f32"),
+                                 ring=True)
+    assert_close(dec(out, kv), eo, *bars(kv), what="out")
+    assert_close(lse.cpu().numpy(), el, 5e-3, 1e-3, what="lse")
+
+
 def test_varlen_positions_clamped_to_bound():
     """Positions above q_pos_max act as q_pos_max, negative ones as 0."""
     kv, Lq, H, D, k, W, R, m = "f32", 1, 4, 128, 16, 8, 8, 4
