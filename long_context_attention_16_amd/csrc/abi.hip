@@ -308,7 +308,7 @@ size_t csa_sparse_attn_ws_bytes(int B, int Lq, int H, int D, int topk, int W) {
   const size_t split = attn_ws(B, Lq, H, D, attn_nsplit_max_csa(topk, W), 4);
   // many-head bf16 shapes run the two-launch kernel (the KV dtype is not an
   // argument here, so such shapes get room for both)
-  if (!attn_decode_eligible(CSA_BF16, false, H, D) || topk + W == 0) return split;
+  if (!attn_decode_eligible(CSA_BF16, false, H, D, topk, W)) return split;
   const size_t dec = attn_decode_ws(B, Lq, H, topk, W);
   return split > dec ? split : dec;
 }
@@ -331,7 +331,7 @@ static int sparse_attn(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int 
   a.B = B; a.Lq = Lq; a.q_pos0 = q_pos0; a.q_pos = q_pos; a.m = 1; a.H = H; a.D = D; a.q = q; a.N_cap = N_cap;
   a.k_c = k_c; a.v_c = v_c; a.topk = topk; a.idx = idx; a.T_raw = T_raw; a.raw_pos0 = ring ? 0 : raw_pos0;
   a.ring = ring; a.k_raw = k_raw; a.v_raw = v_raw; a.W = W; a.sink = sink; a.out = out; a.lse = lse;
-  if (attn_decode_eligible(kv_dtype, false, H, D) && topk + W > 0)
+  if (attn_decode_eligible(kv_dtype, false, H, D, topk, W))
     return launch_attn_decode(a, ws, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
   a.nsplit_max = attn_nsplit_max_csa(topk, W);
   const size_t slots = (size_t)B * Lq * a.nsplit_max * H;

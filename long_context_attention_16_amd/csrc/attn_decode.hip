@@ -435,8 +435,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
 
 }  // namespace
 
-bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D) {
-  return !hca && kv_dtype == 1 && D == kDecD && H % 16 == 0 && H >= 16 && H <= 128;
+// Sources per query must also fit phase B's table of chunk statistics
+// (kMaxChunks chunks); the API allows more (W up to 1024), and such calls run
+// the general split kernel.
+bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D, int topk, int W) {
+  return !hca && kv_dtype == 1 && D == kDecD && H % 16 == 0 && H >= 16 && H <= 128 && topk + W > 0 &&
+         topk + W <= kMaxChunks * kArows;
 }
 
 int attn_decode_chunks(int topk, int W) { return (topk + W + kArows - 1) / kArows; }

@@ -105,7 +105,7 @@ size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk);
 // CSA attention in two launches for one bf16 KV head of dim 512 and H a
 // multiple of 16 (attn_decode.hip); ws holds the bf16 P' rows and the chunk
 // statistics, attn_decode_ws bytes.
-bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D);
+bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D, int topk, int W);
 size_t attn_decode_ws(int B, int Lq, int H, int topk, int W);
 int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st);
 int launch_index_qk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,

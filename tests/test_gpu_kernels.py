@@ -250,6 +250,8 @@ def test_sparse_attn(fmt, B, Lq, H, D, k, W, sink):
     (2, 2, 48, 200, 128, 50, True),        # window cut at t = 50 < W, padded idx
     (1, 2, 128, 300, 40, 5000, False),     # 128 heads, no sink
     (3, 1, 16, 64, 0, 900, True),          # compressed only
+    (1, 2, 16, 2048, 256, 9000, True),     # 2304 sources: the most the two-launch path takes
+    (1, 2, 16, 2048, 300, 9000, True),     # 2348 sources: beyond it, the general split kernel
 ])
 def test_sparse_attn_many_heads(B, Lq, H, k, W, q_pos0, sink):
     # bf16, D = 512, H a multiple of 16: the two-launch path (logits, then P V per D slice)
