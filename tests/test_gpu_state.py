@@ -236,6 +236,8 @@ def _attn_case(kv, B, Lq, H, D, N_cap, R, seed):
     ("bf16", 1, 64, 512, 512, 128, 128),   # the two-launch decode kernel
     ("bf16", 2, 32, 512, 200, 100, 105),   # a ring a little longer than the windows
     ("f32", 3, 4, 128, 64, 16, 20),        # the split-KV kernel
+    ("bf16", 1, 16, 512, 2048, 256, 260),  # 2304 sources: the most the two-launch kernel takes
+    ("bf16", 1, 16, 512, 2048, 400, 400),  # 2448 sources: the split-KV kernel over the rings
 ])
 def test_sparse_attn_varlen(kv, Lq, H, D, k, W, R):
     B, m = 4, 4
