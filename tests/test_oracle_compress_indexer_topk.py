@@ -162,3 +162,44 @@ def test_topk_batch_visibility_and_padding():
     assert idx[0, 0].tolist() == [0, 1, -1, -1]
     idx = topk_batch(s[:, 1:], 2, q_pos0=11, m=4)
     assert idx[0, 0].tolist() == [0, 1]
+
+
+def test_topk_bf16_worked_rows():
+    """[P1] section FP4 量化: indexer scores rounded from FP32 to BF16 before the
+    top-k. Expected selections worked by hand from the bf16 grid (8 significant
+    bits: spacing 2^-7 on [1, 2)), with ties between equal rounded scores going
+    to the lower index. Sequence 0 sees 7 entries (position 6, m = 1), sequence
+    1 sees 6 (position 5); the entries past them hold NaN / -inf and are never
+    read."""
+    from oracle.topk import topk_batch_bf16
+    e = 2.0 ** -10
+    row0 = [0.5,                 # -> 0.5
+            1.0,                 # -> 1.0
+            2.0,                 # -> 2.0
+            1.0 + e,             # below the midpoint 1 + 2^-8: -> 1.0
+            1.0 + 2.0 ** -8,     # the midpoint itself: ties to the even code, 1.0
+            1.0 + 3 * 2.0 ** -8,  # midpoint of 1 + 2^-7 (odd) and 1 + 2^-6 (even): -> 1.015625
+            1.0 + 2.0 ** -7 - e,  # above the midpoint 1 + 2^-8: -> 1.0078125
+            float("nan")]        # invisible
+    row1 = [-1.0 - e,            # -> -1.0, ties with entry 1
+            -1.0,
+            -0.0,                # -0 counts as +0
+            2.0 ** -140,         # far below bf16's smallest subnormal 2^-133: -> +0
+            0.0,
+            -2.0,
+            -float("inf"),       # invisible
+            float("nan")]        # invisible
+    scores = np.array([[row0], [row1]], dtype=np.float64)
+    idx = topk_batch_bf16(scores, 4, np.array([6, 5]), 1)
+    # row 0 rounded: [0.5, 1, 2, 1, 1, 1.015625, 1.0078125]; by (-r, j): 2, 5, 6, then 1
+    assert idx[0, 0].tolist() == [1, 2, 5, 6]
+    # row 1 rounded: [-1, -1, 0, 0, 0, -2]; by (-r, j): 2, 3, 4, then 0
+    assert idx[1, 0].tolist() == [0, 2, 3, 4]
+    # the f32 order would differ in both rows (a selection made before rounding)
+    from oracle.topk import topk_batch
+    f32 = topk_batch(np.where(np.isfinite(scores), scores, 0.0), 4, np.array([6, 5]), 1)
+    assert f32[0, 0].tolist() == [2, 4, 5, 6] and f32[1, 0].tolist() == [1, 2, 3, 4]
+    # fewer visible entries than k: every one, then -1 padding
+    idx = topk_batch_bf16(scores, 8, np.array([6, 5]), 1)
+    assert idx[0, 0].tolist() == [0, 1, 2, 3, 4, 5, 6, -1]
+    assert idx[1, 0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
