@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum {
   CSA_F32 = 0,
@@ -76,13 +76,24 @@ int csa_abi_version(void);
 const char* csa_strerror(int code);
 
 /*
- * csa_compress — fold every m raw tokens' K and V into one compressed entry.
+ * csa_compress — fold every m raw tokens' K and V (and optionally the
+ * indexer's raw keys) into one compressed entry.
  * [P1] 混合注意力機制: CSA compresses each m = 4 tokens' KV cache into one
- * entry (sequence length 1/m); HCA uses m' = 128. Form taken (the pages give
- * none): a softmax-gated weighted sum. For the block j of absolute positions
- * s = j*m .. j*m+m-1:
+ * entry (sequence length 1/m) and its light indexer picks among those
+ * compressed blocks; HCA uses m' = 128. [P1] FP4 量化: the indexer's QK path
+ * runs in FP4. Form taken (the pages give none): a softmax-gated weighted
+ * sum. For the block j of absolute positions s = j*m .. j*m+m-1:
  *   g_s = <w_gate, K_raw[s]>,  alpha = softmax_s(g),
- *   K_c[j] = RoPE(sum_s alpha_s K_raw[s], j*m+m-1),  V_c[j] = sum_s alpha_s V_raw[s].
+ *   K_c[j] = RoPE(sum_s alpha_s K_raw[s], j*m+m-1),  V_c[j] = sum_s alpha_s V_raw[s],
+ *   KI_c[j] = sum_s alpha_s KI_raw[s]   (unrotated: the indexer has no RoPE),
+ * KI_c stored in idx_dtype as csa_state_append stores it: f32; bf16 (nearest
+ * even); e4m3fn (nearest even, magnitudes above 448 saturate to 448); MXFP4
+ * (per 32 elements the e8m0 code floor(log2 amax) - 2 + 127 clamped to
+ * 0..254, 0 for an all-zero block; elements nearest e2m1, ties to the even
+ * code, saturating at 6; sign bits copied).
+ * RoPE angles are computed inside the kernels (position times frequency
+ * reduced to a fraction of a revolution in double precision, then sin/cos in
+ * float on [-pi, pi]), so no cos/sin table is passed.
  *
  *   B, T, D      sequences, raw tokens per sequence, head dim (128 or 512)
  *   m            block size, 1..4096
@@ -93,10 +104,17 @@ const char* csa_strerror(int code);
  *   k_c, v_c     [B, N_cap, D]; rows pos0/m .. pos0/m + T/m - 1 are written,
  *                others untouched. A trailing partial block (T % m tokens)
  *                produces nothing. Requires pos0/m + T/m <= N_cap.
+ *   d_i          0 (no indexer key) or 32, 64, 128
+ *   idx_dtype    storage of ki_c (any csa_dtype; ignored when d_i = 0)
+ *   ki_raw       [B, T, d_i] raw indexer keys in kv_dtype (d_i > 0)
+ *   ki_c         [B, N_cap, d_i] (fp4: [B, N_cap, d_i/2] bytes), the same rows
+ *                as k_c written; ki_c_scale [B, N_cap, d_i/32] e8m0 (fp4 only)
  */
 int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
                  const void* k_raw, const void* v_raw, const float* w_gate,
-                 void* k_c, void* v_c, int64_t N_cap, void* stream);
+                 void* k_c, void* v_c, int64_t N_cap,
+                 int d_i, int idx_dtype, const void* ki_raw, void* ki_c, uint8_t* ki_c_scale,
+                 void* stream);
 
 /*
  * csa_index_topk — Lightning Indexer scores, then per-query top-k.

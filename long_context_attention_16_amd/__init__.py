@@ -22,7 +22,7 @@ _I, _L, _P, _Z = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 SIGNATURES = {
     "csa_abi_version": (_I, []),
     "csa_strerror": (ctypes.c_char_p, [_I]),
-    "csa_compress": (_I, [_I, _I, _I, _I, _L, _I, _P, _P, _P, _P, _P, _L, _P]),
+    "csa_compress": (_I, [_I, _I, _I, _I, _L, _I, _P, _P, _P, _P, _P, _L, _I, _I, _P, _P, _P, _P]),
     "csa_index_topk_ws_bytes": (_Z, [_I, _I, _L, _I, _L, _I]),
     "csa_topk_ws_bytes": (_Z, [_I, _I, _L, _I, _I]),
     "csa_index_topk": (_I, [_I, _I, _L, _I, _L, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P, _Z, _P]),
@@ -165,17 +165,36 @@ def _attn_shapes(q, k_c, v_c, k_raw, v_raw, sink, out=None, lse=None):
 
 
 # ------------------------------------------------------------------ compress
-def compress(k_raw, v_raw, w_gate, m, pos0, k_c, v_c):
+def compress(k_raw, v_raw, w_gate, m, pos0, k_c, v_c, ki_raw=None, ki_c=None, ki_scale=None, idx_fmt="bf16"):
     """Fold [B, T, D] raw rows at absolute positions pos0.. into k_c, v_c
-    [B, N_cap, D] (rows pos0//m .. pos0//m + T//m - 1 are written)."""
+    [B, N_cap, D] (rows pos0//m .. pos0//m + T//m - 1 are written). With
+    ki_raw [B, T, d_i] (KV dtype) the indexer keys are folded with the same
+    weights into ki_c [B, N_cap, d_i] in idx_fmt ('f32', 'bf16', 'fp8', or
+    'fp4': [B, N_cap, d_i/2] bytes plus ki_scale [B, N_cap, d_i/32])."""
     B, T, D = k_raw.shape
     _kv_dtype(k_raw)
     _expect(v_raw, k_raw.shape, "v_raw", dtype=k_raw.dtype)
     _expect(w_gate, (D,), "w_gate", dtype=torch.float32)
     _expect(k_c, (B, k_c.shape[1], D), "k_c", dtype=k_raw.dtype)
     _expect(v_c, k_c.shape, "v_c", dtype=k_raw.dtype)
+    d_i = 0
+    if ki_raw is not None:
+        if idx_fmt not in IDX_FORMATS:
+            raise CSAError("unknown indexer format %r" % (idx_fmt,))
+        d_i = ki_raw.shape[-1]
+        _expect(ki_raw, (B, T, d_i), "ki_raw", dtype=k_raw.dtype)
+        fp4 = idx_fmt == "fp4"
+        if ki_c is None:
+            raise CSAError("ki_raw needs ki_c")
+        _expect(ki_c, (B, k_c.shape[1], d_i // 2 if fp4 else d_i), "ki_c", esize=_IDX_ESIZE[idx_fmt])
+        if fp4:
+            if ki_scale is None:
+                raise CSAError("fp4 indexer keys need ki_scale")
+            _expect(ki_scale, (B, k_c.shape[1], d_i // 32), "ki_scale", esize=1)
     _check(lib().csa_compress(B, T, D, m, pos0, _kv_dtype(k_raw), _ptr(k_raw), _ptr(v_raw),
-                              _ptr(w_gate), _ptr(k_c), _ptr(v_c), k_c.shape[1], _stream()))
+                              _ptr(w_gate), _ptr(k_c), _ptr(v_c), k_c.shape[1], d_i, IDX_FORMATS[idx_fmt],
+                              _ptr(ki_raw), _ptr(ki_c if d_i else None), _ptr(ki_scale if d_i else None),
+                              _stream()))
     return k_c, v_c
 
 

@@ -66,17 +66,22 @@ const char* csa_strerror(int code) {
 }
 
 int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
-                 const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
-                 void* stream) {
+                 const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap, int d_i,
+                 int idx_dtype, const void* ki_raw, void* ki_c, uint8_t* ki_c_scale, void* stream) {
   if (!k_raw || !v_raw || !w_gate || !k_c || !v_c) return CSA_ERR_NULL;
+  if (d_i > 0 && (!ki_raw || !ki_c)) return CSA_ERR_NULL;
+  if (d_i > 0 && idx_dtype == CSA_FP4_E2M1 && !ki_c_scale) return CSA_ERR_NULL;
   if (!kv_ok(kv_dtype)) return CSA_ERR_DTYPE;
+  if (d_i > 0 && (idx_dtype < CSA_F32 || idx_dtype > CSA_FP4_E2M1)) return CSA_ERR_DTYPE;
   if (B < 0 || T < 0 || !head_dim_ok(D) || m < 1 || m > 4096 || pos0 < 0 || pos0 % m != 0 || N_cap < 0)
     return CSA_ERR_SHAPE;
+  if (!(d_i == 0 || d_i == 32 || d_i == 64 || d_i == 128)) return CSA_ERR_SHAPE;
   if (pos0 / m + T / m > N_cap) return CSA_ERR_SHAPE;
-  if (!aligned16(k_raw) || !aligned16(v_raw) || !aligned16(w_gate) || !aligned16(k_c) || !aligned16(v_c))
+  if (!aligned16(k_raw) || !aligned16(v_raw) || !aligned16(w_gate) || !aligned16(k_c) || !aligned16(v_c) ||
+      (d_i > 0 && (!aligned16(ki_raw) || !aligned16(ki_c))))
     return CSA_ERR_ALIGN;
-  return launch_compress(B, T, D, m, pos0, kv_dtype, k_raw, v_raw, w_gate, k_c, v_c, N_cap,
-                         as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
+  return launch_compress(B, T, D, m, pos0, kv_dtype, k_raw, v_raw, w_gate, k_c, v_c, N_cap, d_i, idx_dtype,
+                         ki_raw, ki_c, ki_c_scale, as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
 size_t csa_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
@@ -438,6 +443,7 @@ static int attn_bwd(int B, int Lq, int64_t q_pos0, int m, int H, int D, int kv_d
   // pairs are indexed as qrow * topk + slot in 32 bits
   if (!hca && (int64_t)B * Lq * topk >= ((int64_t)1 << 31)) return CSA_ERR_SHAPE;
   const int64_t S = bwd_slots(Lq, q_pos0, m, topk, W);
+  if (S > ((int64_t)1 << 30)) return CSA_ERR_SHAPE;  // slots are counted in 32 bits
   if (!ws || ws_bytes < csa_sparse_attn_bwd_ws_bytes(B, Lq, q_pos0, m, H, D, N_cap, topk, W))
     return CSA_ERR_WORKSPACE;
   AttnArgs a{};

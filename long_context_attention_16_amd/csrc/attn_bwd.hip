@@ -441,11 +441,7 @@ __global__ __launch_bounds__(2 * kWave) void attn_bwd_q_mfma_kernel(AttnBwdArgs 
     const bool win = si.n_w > 0 && ts + 32 > si.n_c;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(LOADS));  // this tile's copies (the next tile's may fly)
     attn_lds_barrier();
-#ifdef NOROPE
-    if (false) {
-#else
     if (win) {  // window keys rotated in LDS; thread t always takes pair t % 32
-#endif
       for (int e = tid; e < 32 * kRopePairs; e += NT) {
         const int r = e / kRopePairs, pr = e % kRopePairs;
         if (kind[bi][r] != 2) continue;
@@ -1015,7 +1011,8 @@ int launch_attn_bwd(const AttnArgs& a, bool hca, int S, int kv_dtype, const void
     }
 #undef CSA_BWD_KV
   }
-  if (dsink && rows > 0) hipLaunchKernelGGL(dsink_sum_kernel, dim3(a.H), dim3(256), 0, st, w.dsink_part, rows, a.H, dsink);
+  // with no query rows the kernel writes zeros
+  if (dsink) hipLaunchKernelGGL(dsink_sum_kernel, dim3(a.H), dim3(256), 0, st, w.dsink_part, rows, a.H, dsink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

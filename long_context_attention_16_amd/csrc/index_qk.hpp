@@ -28,11 +28,7 @@
 namespace csa {
 
 constexpr int kIdxWaves = 4;
-#ifdef CSA_IDX_TILES_PER_WAVE
-constexpr int kIdxTilesPerWave = CSA_IDX_TILES_PER_WAVE;
-#else
 constexpr int kIdxTilesPerWave = 16;
-#endif
 constexpr int kIdxColsPerWG = kIdxWaves * kIdxTilesPerWave * 32;  // entries per workgroup
 
 // Operand fragment of one MFMA k-step for one lane, by format. The order in
@@ -122,13 +118,7 @@ template <> struct IdxOp<3> {  // MXFP4: 32 e2m1 codes (16 bytes) at 64s + 32*ha
 // deeper rings keep more bytes in flight per wave but lengthen the ring's
 // fill and drain at the ends of each wave's tile chain, and the HBM system is
 // already saturated at this occupancy (two waves per SIMD).
-template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() {
-#ifdef CSA_IDX_NBUF
-  return CSA_IDX_NBUF;
-#else
-  return 2;
-#endif
-}
+template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() { return 2; }
 
 // Scores for one group of queries (MTILES*32 rows = G queries x HI heads)
 // against the kIdxColsPerWG entries of chunk c. Wave w takes the 32-entry

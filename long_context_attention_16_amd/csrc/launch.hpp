@@ -68,9 +68,11 @@ __host__ __device__ inline int attn_nsplit(int S) {
   return ns < 1 ? 1 : ns;
 }
 
+// d_i > 0: also fold the raw indexer keys ki_raw [B, T, d_i] (KV dtype) into
+// ki_c [B, N_cap, d_i] in idx_fmt (+ e8m0 scales for MXFP4).
 int launch_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype, const void* k_raw,
-                    const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap,
-                    hipStream_t stream);
+                    const void* v_raw, const float* w_gate, void* k_c, void* v_c, int64_t N_cap, int d_i,
+                    int idx_fmt, const void* ki_raw, void* ki_c, uint8_t* ki_c_scale, hipStream_t stream);
 // One decode step of the state cache (ring append + completed-block compression).
 int launch_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* pos, const void* k_new,
                         const void* v_new, const float* w_gate, void* k_ring, void* v_ring, void* k_c, void* v_c,

@@ -138,8 +138,20 @@ size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk) {
   return (size_t)rows * topk * 8 * ((size_t)nlists + (nlists + G - 1) / G);
 }
 
+// idx[i] = -1 for i < n: the output of rows that see no entry yet (a fill
+// kernel rather than a memset, so a captured graph replays it as it is).
+__global__ __launch_bounds__(256) void fill_pad_kernel(int32_t* __restrict__ idx, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) idx[i] = -1;
+}
+
 int launch_topk_merge(int64_t rows, int nlists, int topk, void* lists, int32_t* idx_out, hipStream_t stream) {
-  if (rows == 0 || nlists == 0) return 0;
+  if (rows == 0) return 0;
+  if (nlists == 0) {  // no row has a visible entry: every slot is padding
+    const int64_t n = rows * topk;
+    const int nb = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(fill_pad_kernel, dim3(nb), dim3(256), 0, stream, idx_out, n);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+  }
   const int G = topk_group(topk);
   // two ping-pong regions: level 0 (nlists lists per row) and level 1 (ceil(nlists/G))
   const int n1 = (nlists + G - 1) / G;

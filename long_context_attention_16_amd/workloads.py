@@ -158,6 +158,16 @@ def make_inputs(s: CSAShape, seed: int, device="cpu"):
     return out
 
 
+def chunk_index_keys(s: CSAShape, seed: int, device="cpu"):
+    """Raw indexer keys [B, T_comp, d_I] of the tokens a prefill step
+    compresses (KV dtype): integers in {-2..2} for exact shapes, else N(0, 1).
+    Their folds become the chunk's compressed indexer keys."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 7919)
+    draw = _int_values if s.exact else _normal
+    return _store(draw((s.B, s.T_comp, s.d_I), gen, device), s.kv)
+
+
 def small_shape(**kw):
     """A CSAShape for tests with defaults that fit the oracle in seconds."""
     base = dict(name="small", B=2, Lq=8, q_pos0=200, H=4, D=128, m=4, N_cap=64, W=16,

@@ -3,6 +3,7 @@ import numpy as np
 import torch
 
 from oracle import formats
+from oracle import formats as ofmt
 
 
 def dec(t, fmt, scale=None):
@@ -59,3 +60,66 @@ def topk_matches_up_to_ties(gpu_idx, scores, k, rtol=1e-5):
     for j in diff:
         assert abs(s[j] - thr) <= tol, "top-k differs at j=%d beyond a near-tie (%.9g vs %.9g)" % (j, s[j], thr)
     return len(diff)
+
+
+def ki_alloc(B, N_cap, d_i, idx_fmt, DEV="cuda"):
+    """Compressed indexer-key buffers (and MXFP4 scales) filled with a marker."""
+    if idx_fmt == "f32":
+        return torch.full((B, N_cap, d_i), 7.0, device=DEV), None
+    if idx_fmt == "bf16":
+        return torch.full((B, N_cap, d_i), 7.0, device=DEV).to(torch.bfloat16), None
+    if idx_fmt == "fp8":
+        return torch.full((B, N_cap, d_i), 0x77, dtype=torch.uint8, device=DEV), None
+    return (torch.full((B, N_cap, d_i // 2), 0x77, dtype=torch.uint8, device=DEV),
+            torch.full((B, N_cap, d_i // 32), 0x77, dtype=torch.uint8, device=DEV))
+
+
+def codes_ok(got_codes, x, enc, eps=1e-4):
+    """Every GPU code equals the oracle's encoding of x or, where x lies
+    within a relative eps of a rounding boundary, of x scaled by 1 +- eps
+    (the f32 fold and the fp64 oracle may land on either side)."""
+    got = np.asarray(got_codes).astype(np.int64)
+    ok = np.zeros(got.shape, dtype=bool)
+    for f in (1.0, 1.0 - eps, 1.0 + eps):
+        ok |= got == enc(x * f).astype(np.int64)
+    return ok
+
+
+def check_ki(ki_c, ki_sc, want, idx_fmt, kv_fmt, rows, exact=False):
+    """Compare the written indexer-key rows [(b, j)] with the oracle fold.
+    exact: the fold is exact on the GPU too (m = 1: the row itself), so every
+    code must be the oracle's encoding of it, bit for bit."""
+    if idx_fmt == "f32":
+        got = dec(ki_c, idx_fmt)
+        for b, j in rows:
+            assert_close(got[b, j], want[b, j], 1e-4, 1e-5, what="ki_c")
+        return
+    if idx_fmt == "bf16":
+        # a stored rounding: each bf16 code is the oracle's nearest-even code
+        # (within the rounding-boundary rule of codes_ok)
+        got = ki_c.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        eps = 0.0 if exact else 1e-3 if kv_fmt == "bf16" else 1e-4
+        for b, j in rows:
+            ok = codes_ok(got[b, j], want[b, j], ofmt.f64_to_bf16, eps=eps)
+            assert ok.all(), "bf16 indexer key codes differ at b=%d j=%d" % (b, j)
+        return
+    if idx_fmt == "fp8":
+        got = ki_c.cpu().numpy()
+        for b, j in rows:
+            eps = 0.0 if exact else 1e-3 if kv_fmt == "bf16" else 1e-4
+            ok = codes_ok(got[b, j], want[b, j], ofmt.f64_to_e4m3fn, eps=eps)
+            assert ok.all(), "fp8 indexer key codes differ at b=%d j=%d" % (b, j)
+        return
+    packed, sc = ki_c.cpu().numpy(), ki_sc.cpu().numpy()
+    eps = 0.0 if exact else 1e-3 if kv_fmt == "bf16" else 1e-4
+    for b, j in rows:
+        x = want[b, j]
+        codes = ofmt.unpack_fp4(packed[b, j])
+        for blk in range(x.shape[0] // 32):
+            xb = x[32 * blk:32 * blk + 32]
+            cands = {int(ofmt.f64_to_mxfp4(xb * f)[1][0]) for f in (1.0, 1.0 - eps, 1.0 + eps)}
+            s = int(sc[b, j, blk])
+            assert s in cands, "fp4 scale differs at b=%d j=%d block %d" % (b, j, blk)
+            X = 2.0 ** (s - 127)
+            ok = codes_ok(codes[32 * blk:32 * blk + 32], xb / X, ofmt.f64_to_e2m1, eps)
+            assert ok.all(), "fp4 element codes differ at b=%d j=%d block %d" % (b, j, blk)

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     for code in range(7):
         assert len(lib.csa_strerror(code)) > 0
     assert lib.csa_strerror(99) == b"unknown status"
@@ -66,8 +66,21 @@ def test_ws_queries(lib):
 
 def test_compress_rejects(lib):
     f = lib.csa_compress
-    args = [2, 64, 128, 4, 0, 1, P, P, P, P, P, 16, None]
+    args = [2, 64, 128, 4, 0, 1, P, P, P, P, P, 16, 0, 0, None, None, None, None]
     assert f(*args[:6], None, *args[7:]) == NULL
+    # the indexer-key fold: d_i 32/64/128 with its buffers and a valid format
+    fold = list(args); fold[12:17] = [128, 3, P, P, None]
+    assert f(*fold) == NULL                       # MXFP4 without its scale buffer
+    bad = list(fold); bad[14] = None
+    assert f(*bad) == NULL                        # no raw indexer keys
+    bad = list(fold); bad[12] = 48
+    bad[16] = P
+    assert f(*bad) == SHAPE                       # d_i not 32/64/128
+    bad = list(fold); bad[13] = 7
+    assert f(*bad) == DTYPE                       # unknown indexer format
+    bad = list(fold); bad[15] = MIS
+    bad[16] = P
+    assert f(*bad) == ALIGN
     bad = list(args); bad[2] = 256
     assert f(*bad) == SHAPE                       # D not 128/512
     bad = list(args); bad[4] = 2
@@ -227,3 +240,8 @@ def test_attn_bwd_rejects(lib):
     h = lib.hca_dense_attn_bwd
     hb = [1, 1, 1000, 128, 4, 128, 1, P, 6, P, P, 8, 993, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n, None]
     assert h(*hb) == SHAPE                        # n(1000) = 7 entries need N_cap >= 7
+    # HCA slots n(t_last) + W beyond 2^30: rejected before any launch (slots are counted in 32 bits)
+    big = 1 << 30
+    hb2 = [1, 1, big + 5, 1, 4, 128, 1, P, big + 6, P, P, 8, big - 2, P, P, 8, P, P, P, P, P, P, P, P, P, P, P, n,
+           None]
+    assert h(*hb2) == SHAPE

@@ -10,7 +10,7 @@ from oracle import attention as oatt
 from oracle import compress as ocmp
 from oracle import indexer as oidx
 from oracle import topk as otopk
-from helpers import assert_close, dec, kv_fmt
+from helpers import assert_close, check_ki, dec, ki_alloc, kv_fmt
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -61,6 +61,70 @@ def test_compress(fmt, D, m, B, T, pos0, N_cap):
         assert_close(gv[b, r0:r0 + nb], ev, *bars(fmt), what="v_c b=%d" % b)
     # rows outside the written range are untouched
     assert np.all(gk[:, :r0] == 7.0) and np.all(gk[:, r0 + nb:] == 7.0)
+
+
+@pytest.mark.parametrize("kv,D,m,B,T,pos0,N_cap,idx_fmt,d_i", [
+    ("bf16", 128, 4, 1, 4096, 61440, 16384, "fp8", 32),   # the prefill chunk's indexer keys
+    ("bf16", 512, 4, 2, 200, 8, 60, "bf16", 128),
+    ("f32", 128, 7, 2, 100, 14, 40, "f32", 64),           # a partial last quad of rows
+    ("bf16", 128, 4, 3, 130, 0, 40, "fp4", 128),          # two tail tokens make no entry
+    ("bf16", 512, 128, 1, 384, 128, 4, "fp4", 64),        # the HCA block
+    ("f32", 512, 4, 1, 64, 0, 16, "fp8", 128),
+])
+def test_compress_index_key(kv, D, m, B, T, pos0, N_cap, idx_fmt, d_i):
+    """The indexer-key fold of the batch compressor: the raw indexer keys of
+    each block folded with the block's own softmax weights (unrotated), stored
+    in the indexer's format; K and V as in test_compress."""
+    g = _gen(13 + D + m + d_i)
+    dt = torch.float32 if kv == "f32" else torch.bfloat16
+    k = torch.randn((B, T, D), generator=g, device=DEV).to(dt)
+    v = torch.randn((B, T, D), generator=g, device=DEV).to(dt)
+    x = torch.randn((B, T, d_i), generator=g, device=DEV).to(dt)
+    w = (torch.randn((D,), generator=g, device=DEV) / D ** 0.5).contiguous()
+    kc = torch.full((B, N_cap, D), 7.0, device=DEV).to(dt)
+    vc = torch.full((B, N_cap, D), 7.0, device=DEV).to(dt)
+    ki_c, ki_sc = ki_alloc(B, N_cap, d_i, idx_fmt)
+    mark = ki_c.clone()
+    csa.compress(k, v, w, m, pos0, kc, vc, ki_raw=x, ki_c=ki_c, ki_scale=ki_sc, idx_fmt=idx_fmt)
+    torch.cuda.synchronize()
+    K, V, X, Wg = dec(k, kv), dec(v, kv), dec(x, kv), dec(w, "f32")
+    r0, nb = pos0 // m, T // m
+    want_x = np.zeros((B, N_cap, d_i))
+    gk, gv = dec(kc, kv), dec(vc, kv)
+    for b in range(B):
+        ek, ev, ex = ocmp.compress(K[b], V[b], Wg, m, pos0, x_raw=X[b])
+        assert_close(gk[b, r0:r0 + nb], ek, *bars(kv), what="k_c b=%d" % b)
+        assert_close(gv[b, r0:r0 + nb], ev, *bars(kv), what="v_c b=%d" % b)
+        want_x[b, r0:r0 + nb] = ex
+    rows = [(b, j) for b in range(B) for j in range(r0, r0 + nb)]
+    check_ki(ki_c, ki_sc, want_x, idx_fmt, kv, rows)
+    # rows outside the written range are untouched
+    assert torch.equal(ki_c[:, :r0], mark[:, :r0]) and torch.equal(ki_c[:, r0 + nb:], mark[:, r0 + nb:])
+
+
+@pytest.mark.parametrize("kv,D,idx_fmt,d_i", [("bf16", 128, "fp8", 32), ("f32", 512, "fp4", 128),
+                                              ("bf16", 512, "bf16", 64), ("f32", 128, "fp4", 64)])
+def test_compress_index_key_exact_m1(kv, D, idx_fmt, d_i):
+    # m = 1: each entry is its own row (softmax weight exactly 1), so every
+    # code is the oracle encoder's, bit for bit
+    g = _gen(17 + d_i)
+    dt = torch.float32 if kv == "f32" else torch.bfloat16
+    B, T, N_cap = 2, 37, 40
+    k = torch.randn((B, T, D), generator=g, device=DEV).to(dt)
+    v = torch.randn((B, T, D), generator=g, device=DEV).to(dt)
+    x = (torch.randn((B, T, d_i), generator=g, device=DEV) * 3.0).to(dt)
+    w = (torch.randn((D,), generator=g, device=DEV) / D ** 0.5).contiguous()
+    kc = torch.zeros((B, N_cap, D), device=DEV).to(dt)
+    vc = torch.zeros_like(kc)
+    ki_c, ki_sc = ki_alloc(B, N_cap, d_i, idx_fmt)
+    csa.compress(k, v, w, 1, 3, kc, vc, ki_raw=x, ki_c=ki_c, ki_scale=ki_sc, idx_fmt=idx_fmt)
+    torch.cuda.synchronize()
+    want = np.zeros((B, N_cap, d_i))
+    want[:, 3:3 + T] = dec(x, kv)
+    if idx_fmt == "bf16":
+        # bf16 KV rows stored as bf16: the very same bits
+        assert torch.equal(ki_c[:, 3:3 + T], x)
+    check_ki(ki_c, ki_sc, want, idx_fmt, kv, [(b, j) for b in range(B) for j in range(3, 3 + T)], exact=True)
 
 
 # ------------------------------------------------------------------ indexer
@@ -131,6 +195,30 @@ def test_index_prefill_fp8_exact(B, Lq, m, q_pos0, n_extra, topk):
     # the many-query fp8 kernel (64 heads x 128, at least 16 query rows)
     N_cap = (q_pos0 + Lq) // m + n_extra
     _index_exact_case("fp8", 64, 128, B, Lq, q_pos0, m, N_cap, topk, seed=Lq + m)
+
+
+@pytest.mark.parametrize("H_i,d_i,Lq,q_pos0", [(64, 128, 1, 0), (64, 128, 1, 2), (128, 64, 1, 1),
+                                               (4, 32, 3, 0)])
+def test_index_topk_no_visible_entry(H_i, d_i, Lq, q_pos0):
+    """Queries that see no compressed entry yet (t < m - 1): every slot is -1
+    padding, on the fused path (one query per workgroup), its two launches
+    called alone, and the score path (4 heads, 3 query rows)."""
+    B, m, topk, N_cap = 2, 4, 512, 64
+    x = _exact_indexer(B, Lq, H_i, d_i, N_cap, "bf16", seed=5 + q_pos0)
+    out = torch.full((B, Lq, topk), 12345, dtype=torch.int32, device=DEV)
+    csa.index_topk(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, "bf16", out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == -1)
+    if Lq == 1:
+        cand = csa.index_candidates(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, "bf16")
+        out2 = torch.full((B, Lq, topk), 12345, dtype=torch.int32, device=DEV)
+        csa.topk_merge(cand, B, Lq, topk, q_pos0, m, out=out2)
+        # per-sequence positions bounded below m - 1
+        q_pos = torch.tensor([q_pos0, 0], dtype=torch.int64, device=DEV)
+        out3 = torch.full((B, Lq, topk), 12345, dtype=torch.int32, device=DEV)
+        csa.index_topk_varlen(x["q_i"], x["w_i"], x["k_i"], topk, q_pos, 2, m, "bf16", out=out3)
+        torch.cuda.synchronize()
+        assert torch.all(out2 == -1) and torch.all(out3 == -1)
 
 
 # -------------------------------------------------------------------- top-k

@@ -16,6 +16,7 @@ from oracle import indexer as oidx
 from oracle import state as ostate
 from oracle import topk as otopk
 from helpers import assert_close, dec, topk_matches_up_to_ties
+from helpers import check_ki as _check_ki, ki_alloc as _ki_alloc
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -35,56 +36,6 @@ def _gen(seed):
 
 def _dt(fmt):
     return torch.float32 if fmt == "f32" else torch.bfloat16
-
-
-def _ki_alloc(B, N_cap, d_i, idx_fmt):
-    if idx_fmt == "f32":
-        return torch.full((B, N_cap, d_i), 7.0, device=DEV), None
-    if idx_fmt == "bf16":
-        return torch.full((B, N_cap, d_i), 7.0, device=DEV).to(torch.bfloat16), None
-    if idx_fmt == "fp8":
-        return torch.full((B, N_cap, d_i), 0x77, dtype=torch.uint8, device=DEV), None
-    return (torch.full((B, N_cap, d_i // 2), 0x77, dtype=torch.uint8, device=DEV),
-            torch.full((B, N_cap, d_i // 32), 0x77, dtype=torch.uint8, device=DEV))
-
-
-def _codes_ok(got_codes, x, enc, eps=1e-4):
-    """Every GPU code equals the oracle's encoding of x or, where x lies
-    within a relative eps of a rounding boundary, of x scaled by 1 +- eps
-    (the f32 fold and the fp64 oracle may land on either side)."""
-    got = np.asarray(got_codes).astype(np.int64)
-    ok = np.zeros(got.shape, dtype=bool)
-    for f in (1.0, 1.0 - eps, 1.0 + eps):
-        ok |= got == enc(x * f).astype(np.int64)
-    return ok
-
-
-def _check_ki(ki_c, ki_sc, want, idx_fmt, kv_fmt, rows):
-    """Compare the written indexer-key rows [(b, j)] with the oracle fold."""
-    if idx_fmt in ("f32", "bf16"):
-        got = dec(ki_c, idx_fmt)
-        for b, j in rows:
-            assert_close(got[b, j], want[b, j], *bars(idx_fmt if kv_fmt == "f32" else "bf16"), what="ki_c")
-        return
-    if idx_fmt == "fp8":
-        got = ki_c.cpu().numpy()
-        for b, j in rows:
-            ok = _codes_ok(got[b, j], want[b, j], ofmt.f64_to_e4m3fn, eps=1e-3 if kv_fmt == "bf16" else 1e-4)
-            assert ok.all(), "fp8 indexer key codes differ at b=%d j=%d" % (b, j)
-        return
-    packed, sc = ki_c.cpu().numpy(), ki_sc.cpu().numpy()
-    eps = 1e-3 if kv_fmt == "bf16" else 1e-4
-    for b, j in rows:
-        x = want[b, j]
-        codes = ofmt.unpack_fp4(packed[b, j])
-        for blk in range(x.shape[0] // 32):
-            xb = x[32 * blk:32 * blk + 32]
-            cands = {int(ofmt.f64_to_mxfp4(xb * f)[1][0]) for f in (1.0, 1.0 - eps, 1.0 + eps)}
-            s = int(sc[b, j, blk])
-            assert s in cands, "fp4 scale differs at b=%d j=%d block %d" % (b, j, blk)
-            X = 2.0 ** (s - 127)
-            ok = _codes_ok(codes[32 * blk:32 * blk + 32], xb / X, ofmt.f64_to_e2m1, eps)
-            assert ok.all(), "fp4 element codes differ at b=%d j=%d block %d" % (b, j, blk)
 
 
 @pytest.mark.parametrize("kv,D,m,R,idx_fmt,d_i", [
