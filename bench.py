@@ -518,8 +518,9 @@ def bench_prefill(args, torch, csa, wl, dev):
     """One CSA layer on a 4096-token prefill chunk at positions 61440..65535
     of a 64K context (config-3 shapes: bf16 KV, H = 4, D = 128, 16384
     compressed entries, literal fp8 indexer 4 x 32, top-1024, W = 128, N(0,1)
-    inputs): csa_compress folds the chunk's own 4096 tokens into entries
-    15360..16383, csa_index_topk selects, csa_sparse_attn attends. Step time:
+    inputs): csa_compress folds the chunk's own 4096 tokens (K, V and the
+    indexer keys, stored as e4m3fn) into entries 15360..16383, csa_index_topk
+    scores those and the earlier entries and selects, csa_sparse_attn attends. Step time:
     HIP-graph replays of the three calls, two input sets alternating; per-call
     times: back-to-back launches between HIP events."""
     from dataclasses import replace
@@ -530,6 +531,7 @@ def bench_prefill(args, torch, csa, wl, dev):
         x = wl.make_inputs(s, sd, device=dev)
         x["kraw_chunk"] = x["k_raw"][:, chunk].contiguous()
         x["vraw_chunk"] = x["v_raw"][:, chunk].contiguous()
+        x["kiraw_chunk"] = wl.chunk_index_keys(s, sd, dev)
         nb = csa.index_topk_ws_bytes(s.B, s.Lq, s.q_pos0, s.m, s.N_cap, s.topk)
         x["tws"] = torch.empty((nb + 15) // 16 * 4, dtype=torch.float32, device=dev)
         x["idx"] = torch.empty((s.B, s.Lq, s.topk), dtype=torch.int32, device=dev)
@@ -542,7 +544,8 @@ def bench_prefill(args, torch, csa, wl, dev):
 
     calls = {
         "compress": lambda x: csa.compress(x["kraw_chunk"], x["vraw_chunk"], x["w_gate"], s.m, s.comp_pos0,
-                                           x["k_c"], x["v_c"]),
+                                           x["k_c"], x["v_c"], ki_raw=x["kiraw_chunk"], ki_c=x["k_i"],
+                                           ki_scale=x["k_i_scale"], idx_fmt=s.idx),
         "index_topk": lambda x: csa.index_topk(x["q_i"], x["w_i"], x["k_i"], s.topk, s.q_pos0, s.m, s.idx,
                                                x["q_i_scale"], x["k_i_scale"], ws=x["tws"], out=x["idx"]),
         "sparse_attn": lambda x: csa.sparse_attn(x["q"], x["k_c"], x["v_c"], x["idx"], x["k_raw"], x["v_raw"],
@@ -584,19 +587,28 @@ def bench_prefill(args, torch, csa, wl, dev):
 
     # algorithmic bytes (every input read once, every output written once)
     D2 = s.D * 2
-    comp_bytes = 2 * s.T_comp * D2 + s.D * 4 + 2 * (s.T_comp // s.m) * D2
+    ki_row = s.d_I * {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 0.5}[s.idx]
+    comp_bytes = (2 * s.T_comp * D2 + s.D * 4 + 2 * (s.T_comp // s.m) * D2 + s.T_comp * s.d_I * 2
+                  + (s.T_comp // s.m) * ki_row)
     vis = sum((s.q_pos0 + i + 1) // s.m for i in range(s.Lq))
     n_last = (s.q_pos0 + s.Lq) // s.m
     topk_bytes = (s.B * n_last * s.d_I + s.B * s.Lq * s.H_I * (s.d_I + 4) + 2 * s.B * vis * 4
                   + s.B * s.Lq * s.topk * 4)
     n_w = sum(min(s.W, s.q_pos0 + i + 1) for i in range(s.Lq))
     rows = s.B * (s.Lq * s.topk + n_w)
-    attn_bytes = rows * 2 * D2 + s.B * s.Lq * s.topk * 4 + 2 * s.B * s.Lq * s.H * D2 + s.B * s.Lq * s.H * 4
-    roof = {"bound": "hbm", "achieved": attn_bytes / (breakdown["sparse_attn"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s"}
+    io_bytes = s.B * s.Lq * s.topk * 4 + 2 * s.B * s.Lq * s.H * D2 + s.B * s.Lq * s.H * 4
+    # rows as gathered, once per query that reads them (most hit L2 / last-level cache) ...
+    gathered = rows * 2 * D2 + io_bytes
+    # ... and the algorithmic bytes: each distinct compressed entry and raw window row read once
+    idx0 = xs[0]["idx"]
+    distinct = sum(int(torch.unique(idx0[b][idx0[b] >= 0]).numel()) for b in range(s.B))
+    win_rows = s.B * (s.Lq + min(s.W, s.q_pos0 + 1) - 1)
+    attn_bytes = (distinct + win_rows) * 2 * D2 + io_bytes
+    t_attn = breakdown["sparse_attn"] * 1e-6
+    roof = {"bound": "hbm", "achieved": attn_bytes / t_attn / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof.update(traffic=None, kernel="sparse_attn (gathered rows counted per query; 35.7 MB of distinct rows, "
-                                     "so most reads hit L2 / last-level cache)", bytes_per_launch=attn_bytes)
+    roof.update(traffic=None, kernel="sparse_attn (distinct rows read once; the gathered rows are served by "
+                                     "L2 / last-level cache, see gather_gbs)", bytes_per_launch=attn_bytes)
     roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
     result = {
         "metric": "CSA prefill query-tok/s (chunk 4096 @64K, compress + index_topk + sparse_attn)",
@@ -611,6 +623,7 @@ def bench_prefill(args, torch, csa, wl, dev):
         "call_gbs": {"compress": round(comp_bytes / (breakdown["compress"] * 1e-6) / 1e9, 1),
                      "index_topk": round(topk_bytes / (breakdown["index_topk"] * 1e-6) / 1e9, 1),
                      "sparse_attn": round(roof["achieved"], 1)},
+        "gather_gbs": round(gathered / t_attn / 1e9, 1),
         "timing": "value/ms_per_step: HIP-graph replays of the three calls; breakdown_us: back-to-back launches "
                   "of each call between HIP events",
         "cpu_baseline": None,
@@ -637,9 +650,11 @@ def _oracle_prefill_baseline(s, x, seconds):
 
     kr_all, vr_all = x["k_raw"][0].cpu(), x["v_raw"][0].cpu()
     kch, vch = x["kraw_chunk"][0].cpu(), x["vraw_chunk"][0].cpu()
+    kich = x["kiraw_chunk"][0].cpu()
     w_gate = x["w_gate"].cpu().numpy().astype(np.float64)
     t0 = time.perf_counter()
-    ocmp.compress(bf(kch), bf(vch), w_gate, s.m, s.comp_pos0)
+    _, _, kic = ocmp.compress(bf(kch), bf(vch), w_gate, s.m, s.comp_pos0, x_raw=bf(kich))
+    formats.f64_to_e4m3fn(kic)
     t_comp = time.perf_counter() - t0
     kc_all, vc_all = x["k_c"][0].cpu(), x["v_c"][0].cpu()
     ki_all = f8(x["k_i"][0].cpu())
@@ -821,6 +836,42 @@ def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
     return round(2 * nbytes / sec / 1e9, 1)
 
 
+def prefill_indexer_mfma(torch, csa, wl, dev, reps=20, warmup=10):
+    """The second half of the headline metric: the fp8 indexer QK of a
+    4096-token prefill chunk at 64K context with 64 heads x 128 dims (the
+    MFMA-bound reading of that workload), as a fraction of the fp8 MFMA peak.
+    Mean of `reps` back-to-back launches between HIP events on the launch
+    stream, after `warmup` launches; two input sets alternate."""
+    s = wl.CFG3M
+    xs = []
+    for sd in (wl.SEEDS["3M"], 1000 + wl.SEEDS["3M"]):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(sd)
+        x = wl.indexer_inputs(s, gen, dev)
+        x["scores"] = torch.empty((s.B, s.Lq, s.N_cap), dtype=torch.float32, device=dev)
+        xs.append(x)
+
+    def launch(x):
+        csa.index_scores(x["q_i"], x["w_i"], x["k_i"], s.q_pos0, s.m, s.idx, x["q_i_scale"], x["k_i_scale"],
+                         out=x["scores"])
+    for k in range(warmup):
+        launch(xs[k % 2])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(reps):
+        launch(xs[k % 2])
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1000.0 * e0.elapsed_time(e1) / reps
+    fl = index_qk_flops(s)
+    tf = fl / (us * 1e-6) / 1e12
+    del xs
+    return {"workload": s.name, "kernel": "index_qk_prefill (fp8 64x128)", "us": round(us, 2),
+            "flops_per_launch": fl, "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4),
+            "timing": "mean of %d back-to-back launches after %d warmup launches" % (reps, warmup)}
+
+
 # ------------------------------------------------------------- CPU baseline
 def _oracle_query(s, x, b):
     """Oracle seconds for query token b of workload s; copying the input rows it
@@ -903,32 +954,57 @@ def _oracle_state_query(s, x, b, t):
     return spent + time.perf_counter() - t0
 
 
-def cpu_baseline(wl_name, parts, seconds, query_fn=None):
-    """Time the CPU oracle, as it stands, on whole query tokens of the same
-    workload (every layer of it) until `seconds` of oracle work have run."""
+def _blas_cores():
     try:
         from threadpoolctl import threadpool_info
         blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = max(blas) if blas else 1
+        return max(blas) if blas else 1
     except Exception:
-        cores = 1
+        return 1
+
+
+def _cpu_model():
+    cpu = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return cpu
+
+
+def _sample(parts, seconds, query_fn):
     B = parts[0][0].B
     done, spent = 0, 0.0
     while done < B and (done == 0 or spent < seconds):
         for s, x in parts:
             spent += query_fn(s, x, done) if query_fn else _oracle_query(s, x, done)
         done += 1
-    cpu = platform.processor() or ""
+    return done, spent
+
+
+def cpu_baseline(wl_name, parts, seconds, query_fn=None):
+    """Time the CPU oracle, as it stands, on whole query tokens of the same
+    workload (every layer of it) until `seconds` of oracle work have run:
+    once with the BLAS threads numpy starts with (all host cores), once with
+    one thread."""
+    cores = _blas_cores()
+    B = parts[0][0].B
+    done, spent = _sample(parts, seconds, query_fn)
+    one = None
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu = line.split(":", 1)[1].strip()
-                break
-    except OSError:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, s1 = _sample(parts, seconds, query_fn)
+        one = {"value": round(d1 / s1, 4), "cores": 1,
+               "sample": "%d of %d query tokens, %.1f s of oracle work" % (d1, B, s1)}
+    except ImportError:
         pass
     return {"value": round(done / spent, 4), "unit": "query-tok/s", "cores": cores, "kind": "oracle",
             "sample": "%d of %d query tokens of %s, %.1f s of oracle work (numpy float64, BLAS threads %d; "
-                      "host has %d CPUs: %s)" % (done, B, wl_name, spent, cores, os.cpu_count(), cpu)}
+                      "host has %d CPUs: %s)" % (done, B, wl_name, spent, cores, os.cpu_count(), _cpu_model()),
+            "one_thread": one}
 
 
 # -------------------------------------------------------------------- main
@@ -1139,6 +1215,8 @@ def main():
         "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
         "copy_ceiling_gbs": copy_ceiling(torch, dev),
     }
+    if W == "csa_decode":
+        result["indexer_mfma"] = prefill_indexer_mfma(torch, csa, wl, dev)
     if args.no_cpu_baseline:
         result["cpu_baseline"] = None
     elif W == "indexer_fp8_prefill":
