@@ -249,6 +249,30 @@ int csa_sparse_attn(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa_sparse_attn_noalloc — csa_sparse_attn for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments, computation and results as
+ * csa_sparse_attn, without ws / ws_bytes: the workspace is a library-owned
+ * device array of CSA_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held until the
+ * process ends; its address is looked up once per device on the first call
+ * with that device current. The call allocates nothing.
+ * Every call on one GPU shares that GPU's array (its contents are whatever
+ * the last call left; nothing needs to start at zero), so calls that overlap
+ * on one GPU (concurrent streams, or host threads without ordering between
+ * their streams) race and must not be made.
+ * Errors: as csa_sparse_attn, plus CSA_ERR_WORKSPACE when
+ * csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W) exceeds the array (checked
+ * before anything is enqueued) and CSA_ERR_LAUNCH when the array's address
+ * cannot be obtained.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa_sparse_attn_noalloc(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype,
+                            const void* q, int64_t N_cap, const void* k_c, const void* v_c,
+                            int topk, const int32_t* idx,
+                            int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                            const float* sink, void* out, float* lse, void* stream);
+
+/*
  * hca_dense_attn — HCA attention: every visible compressed entry plus the
  * sliding window, with attention sink.
  * [P1] 混合注意力機制: HCA compresses 128 tokens into one entry and keeps

@@ -34,6 +34,8 @@ SIGNATURES = {
     "csa_sparse_attn_ws_bytes": (_Z, [_I, _I, _I, _I, _I, _I]),
     "csa_sparse_attn": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
                              _P, _P, _P, _P, _Z, _P]),
+    "csa_sparse_attn_noalloc": (_I, [_I, _I, _L, _I, _I, _I, _P, _L, _P, _P, _I, _P, _I, _L, _P, _P, _I,
+                                     _P, _P, _P, _P]),
     "hca_dense_attn_ws_bytes": (_Z, [_I, _I, _L, _I, _I, _I, _I]),
     "hca_dense_attn": (_I, [_I, _I, _L, _I, _I, _I, _I, _P, _L, _P, _P, _I, _L, _P, _P, _I,
                             _P, _P, _P, _P, _Z, _P]),

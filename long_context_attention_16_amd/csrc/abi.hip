@@ -4,6 +4,8 @@
 #include "../../include/csa.h"
 #include "launch.hpp"
 
+#include <mutex>
+
 using namespace csa;
 
 namespace {
@@ -362,6 +364,51 @@ int csa_sparse_attn_varlen(int B, int Lq, const int64_t* q_pos, int64_t q_pos_ma
   if (!q_pos) return CSA_ERR_NULL;
   return sparse_attn(B, Lq, q_pos_max, q_pos, H, D, kv_dtype, q, N_cap, k_c, v_c, topk, idx, R, 0, k_ring,
                      v_ring, W, sink, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// Workspace of csa_sparse_attn_noalloc: one array per GPU, in the code
+// object's device memory, alive until the process ends. Host code reaches
+// it only through the address hipGetSymbolAddress returns for the current
+// device (the array's name in host code is a host-side stand-in, not a device
+// address). Nothing in it needs to start at zero (the attention kernels
+// write every partial and statistic before reading it).
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's scratch address, looked up once per device (with that
+// device current) and kept; nullptr if the lookup fails.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int csa_sparse_attn_noalloc(int B, int Lq, int64_t q_pos0, int H, int D, int kv_dtype, const void* q,
+                            int64_t N_cap, const void* k_c, const void* v_c, int topk, const int32_t* idx,
+                            int T_raw, int64_t raw_pos0, const void* k_raw, const void* v_raw, int W,
+                            const float* sink, void* out, float* lse, void* stream) {
+  if (B > 0 && Lq > 0 && topk >= 0 && W >= 0 &&
+      csa_sparse_attn_ws_bytes(B, Lq, H, D, topk, W) > (size_t)CSA_NOALLOC_SCRATCH_BYTES)
+    return CSA_ERR_WORKSPACE;  // the call needs more than the fixed scratch
+  void* ws = scratch_address();
+  if (!ws) return CSA_ERR_LAUNCH;
+  return sparse_attn(B, Lq, q_pos0, nullptr, H, D, kv_dtype, q, N_cap, k_c, v_c, topk, idx, T_raw, raw_pos0,
+                     k_raw, v_raw, W, sink, out, lse, ws, CSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t hca_dense_attn_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int H, int D, int W) {
