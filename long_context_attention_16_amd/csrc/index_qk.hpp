@@ -137,44 +137,65 @@ template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() { return 2; }
 // candidate list of k (key, index) pairs per (row, chunk) in ascending index
 // order, padded with key 0 / index -1. The lists of a row are merged by the
 // top-k merge kernel; every entry of the row's top k is in its chunk's top k.
+// LDS of one indexer workgroup (a struct, so that a kernel running several
+// kinds of work can overlay it with the others' in one buffer).
+template <int FMT, int HI, int DI, bool FUSE> struct IdxShared {
+  static constexpr int MTILES = HI == 128 ? 4 : 2;
+  static constexpr int G = MTILES * 32 / HI;  // queries per group
+  typedef IdxOp<FMT> Op;
+  typedef typename Op::Frag Frag;
+  static constexpr int KS = (DI + Op::KW - 1) / Op::KW;
+  static constexpr int kSelThreads = kIdxWaves * kWave;
+  static constexpr int kSelKPT = kIdxColsPerWG / kSelThreads;
+  typedef TopkShared<kSelThreads, kSelKPT> SelShared;
+  static constexpr int kScBytes = (kIdxColsPerWG + kWave) * 4;
+  int s_lim[G];                         // per query: visible entries n(t)
+  float4 s_w[MTILES * 8];               // head weight of each of the MTILES*32 rows
+  Frag s_a[MTILES * KS * kWave];        // q operand fragments
+  uint8_t s_asc[FMT == 3 ? MTILES * KS * kWave : 1];  // their e8m0 scales (fp4)
+  // Fused mode only: the chunk's scores (plus a dump row for masked lanes)
+  // and the selection's scratch, carved from one buffer (16 bytes otherwise).
+  __attribute__((aligned(16))) uint8_t s_fuse[FUSE ? kScBytes + sizeof(SelShared) : 16];
+};
+
+// One indexer work unit: blk is the unit's index (a kernel's block index).
 template <int FMT, int HI, int DI, bool FUSE>
-__global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
+__device__ __forceinline__ void index_qk_body(
+    IdxShared<FMT, HI, DI, FUSE>& S, const int blk,
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
     const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores, int sbf,
     int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
-  constexpr int MTILES = HI == 128 ? 4 : 2;
-  constexpr int G = MTILES * 32 / HI;  // queries per group
+  typedef IdxShared<FMT, HI, DI, FUSE> Sh;
+  constexpr int MTILES = Sh::MTILES;
+  constexpr int G = Sh::G;
   constexpr int NBUF = idx_nbuf<FMT, MTILES, DI>();
   // Padded steps of the ring then only ever fall on tiles past the group's
   // visible entries (stores masked), never past the end of the chunk.
   static_assert(kIdxTilesPerWave % NBUF == 0, "ring depth divides the tiles per wave");
-  constexpr int kSelThreads = kIdxWaves * kWave;
-  constexpr int kSelKPT = kIdxColsPerWG / kSelThreads;
+  constexpr int kSelThreads = Sh::kSelThreads;
+  constexpr int kSelKPT = Sh::kSelKPT;
   typedef IdxOp<FMT> Op;
   typedef typename Op::Frag Frag;
-  constexpr int KS = (DI + Op::KW - 1) / Op::KW;
+  constexpr int KS = Sh::KS;
   constexpr int RB = Op::row_bytes(DI);
   constexpr int SB = DI / 32;  // scale bytes per row (fp4)
   constexpr int NLIM = HI == 4 ? MTILES * 4 : G;  // visibility limits held per lane
-  __shared__ int s_lim[G];                         // per query: visible entries n(t)
-  __shared__ float4 s_w[MTILES * 8];               // head weight of each of the MTILES*32 rows
-  __shared__ Frag s_a[MTILES * KS * kWave];         // q operand fragments
-  __shared__ uint8_t s_asc[FMT == 3 ? MTILES * KS * kWave : 1];  // their e8m0 scales (fp4)
-  // Fused mode only: the chunk's scores (plus a dump row for masked lanes)
-  // and the selection's scratch, carved from one buffer (16 bytes otherwise).
-  typedef TopkShared<kSelThreads, kSelKPT> SelShared;
-  constexpr int kScBytes = (kIdxColsPerWG + kWave) * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t s_fuse[FUSE ? kScBytes + sizeof(SelShared) : 16];
-  float* s_sc = reinterpret_cast<float*>(s_fuse);
-  SelShared& s_sel = *reinterpret_cast<SelShared*>(s_fuse + (FUSE ? kScBytes : 0));
+  int* s_lim = S.s_lim;
+  float4* s_w = S.s_w;
+  Frag* s_a = S.s_a;
+  uint8_t* s_asc = S.s_asc;
+  typedef typename Sh::SelShared SelShared;
+  constexpr int kScBytes = Sh::kScBytes;
+  float* s_sc = reinterpret_cast<float*>(S.s_fuse);
+  SelShared& s_sel = *reinterpret_cast<SelShared*>(S.s_fuse + (FUSE ? kScBytes : 0));
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
   const int l32 = lane % 32;
-  const int c = blockIdx.x % nchunks;  // chunk of kIdxColsPerWG entries
-  const int gg = blockIdx.x / nchunks;
+  const int c = blk % nchunks;  // chunk of kIdxColsPerWG entries
+  const int gg = blk / nchunks;
   const int b = gg / ngroups;
   q_pos0 = seq_pos(q_pos, q_pos0, b);  // from here on: this sequence's row-0 position
   const int i0 = (gg % ngroups) * G;
@@ -392,6 +413,17 @@ __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
     });
     block_select_out(s_sel, topk, oi, ok);
   }
+}
+
+template <int FMT, int HI, int DI, bool FUSE>
+__global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
+    int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
+    const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
+    const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores, int sbf,
+    int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
+  __shared__ IdxShared<FMT, HI, DI, FUSE> S;
+  index_qk_body<FMT, HI, DI, FUSE>(S, blockIdx.x, Lq, q_pos0, q_pos, m, N_cap, ngroups, nchunks, q_i, q_s, w_i, k_i,
+                                   k_s, scores, sbf, topk, cand_key, cand_idx);
 }
 
 // ---------------------------------------------------------------- launch

@@ -253,4 +253,32 @@ __device__ __forceinline__ void block_select_out(TopkShared<THREADS, KPT>& S, in
   }
 }
 
+// The top k of n (key, index) candidates, consecutive lists of k in
+// ascending index order each (a list's position order is index order and
+// lists come in chunk order, so ties still go to the lower index), written as
+// indices to oidx (and keys to okey, if not null) in ascending index order.
+// n <= k passes the candidates through.
+template <int THREADS, int KPT>
+__device__ __forceinline__ void merge_lists(TopkShared<THREADS, KPT>& S, int n, int k, const uint32_t* __restrict__ ik,
+                                            const int32_t* __restrict__ ii, int32_t* __restrict__ oidx,
+                                            uint32_t* __restrict__ okey) {
+  const int tid = threadIdx.x;
+  if (n <= k) {  // a single list passes through
+    for (int p = tid; p < k; p += THREADS) {
+      oidx[p] = ii[p];
+      if (okey) okey[p] = ik[p];
+    }
+    return;
+  }
+  uint32_t key[KPT];
+  int32_t idx[KPT];
+  load_run<KPT>(ik, tid * KPT, n, key);
+  load_run<KPT>(ii, tid * KPT, n, idx);
+  block_select<THREADS, KPT>(key, n, k, S, [&](int slot, int u) {
+    S.hist[slot] = idx[u];
+    S.stage[slot] = key[u];
+  });
+  block_select_out(S, k, oidx, okey);
+}
+
 }  // namespace csa

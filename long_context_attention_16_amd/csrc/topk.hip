@@ -87,32 +87,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(
     int topk, int nlists, int G, const uint32_t* __restrict__ in_key, const int32_t* __restrict__ in_idx,
     int32_t* __restrict__ final_idx, uint32_t* __restrict__ out_key, int32_t* __restrict__ out_idx) {
   __shared__ TopkShared<kTkThreads, KPT> S;
-  const int tid = threadIdx.x;
   const int nout = (nlists + G - 1) / G;
   const int64_t row = blockIdx.x / nout;
   const int grp = (int)(blockIdx.x % nout);
   const int l0 = grp * G;
   const int n = min(G, nlists - l0) * topk;
-  const uint32_t* ik = in_key + (row * nlists + l0) * topk;
-  const int32_t* ii = in_idx + (row * nlists + l0) * topk;
   int32_t* oi = final_idx ? final_idx + row * topk : out_idx + (row * nout + grp) * topk;
   uint32_t* ok = final_idx ? nullptr : out_key + (row * nout + grp) * topk;
-  if (n <= topk) {  // a single list passes through
-    for (int p = tid; p < topk; p += kTkThreads) {
-      oi[p] = ii[p];
-      if (ok) ok[p] = ik[p];
-    }
-    return;
-  }
-  uint32_t key[KPT];
-  int32_t idx[KPT];
-  load_run<KPT>(ik, tid * KPT, n, key);
-  load_run<KPT>(ii, tid * KPT, n, idx);
-  block_select<kTkThreads, KPT>(key, n, topk, S, [&](int slot, int u) {
-    S.hist[slot] = idx[u];
-    S.stage[slot] = key[u];
-  });
-  block_select_out(S, topk, oi, ok);
+  merge_lists<kTkThreads, KPT>(S, n, topk, in_key + (row * nlists + l0) * topk, in_idx + (row * nlists + l0) * topk,
+                               oi, ok);
 }
 
 // Keys per thread of a 1024-thread selection over up to n keys: the work of

@@ -411,6 +411,8 @@ def test_sparse_attn_edges():
     # 15 of 320 at 4609 (the split count is not monotonic in the source
     # count), so the grid must be sized for more splits than the last row's
     ("bf16", 1, 41, 4, 128, 4, 17887, 128),
+    # a decode batch of 8 at 1M context with m' = 128 (16 splits of 544 rows)
+    ("bf16", 8, 1, 64, 512, 128, 1048575, 128),
 ])
 def test_hca_attn(fmt, B, Lq, H, D, m, q_pos0, W):
     N_cap = (q_pos0 + Lq) // m + 1
