@@ -55,10 +55,15 @@ def parse():
 
 
 # --------------------------------------------------------------------------
+def fused_cols(topk):
+    """Entries per chunk of the fused indexer + chunk top-k (0: k too large)."""
+    return 2048 if topk <= 512 else 4096 if topk <= 1024 else 0
+
+
 def fused(s):
     """Whether csa_index_topk runs fused for shape s (one query per indexer
-    workgroup and k at most a quarter of a 2048-entry chunk)."""
-    return (s.H_I >= 64 or s.Lq == 1) and 4 * s.topk <= 2048
+    workgroup and k at most a quarter of a chunk)."""
+    return (s.H_I >= 64 or s.Lq == 1) and fused_cols(s.topk) > 0
 
 
 def csa_decode_setup(torch, csa, wl, shape, seeds, dev):
@@ -122,16 +127,26 @@ def index_cand_bytes(s):
     """Fused indexer: k_I rows, q_I and head weights read once, and the
     per-chunk candidate lists (8 bytes a slot) written once."""
     n_last = (s.q_pos0 + s.Lq) // s.m
-    nchunks = (n_last + 2047) // 2048
+    nchunks = -(-n_last // fused_cols(s.topk))
     kb = s.B * n_last * idx_row_bytes(s)
     qb = s.B * s.Lq * s.H_I * idx_row_bytes(s)
     return kb + qb + s.B * s.Lq * s.H_I * 4 + s.B * s.Lq * nchunks * s.topk * 8
 
 
 def topk_merge_bytes(s):
-    n_last = (s.q_pos0 + s.Lq) // s.m
-    nchunks = (n_last + 2047) // 2048
-    return s.B * s.Lq * nchunks * s.topk * 8 + s.B * s.Lq * s.topk * 4
+    """Merge levels of the fused lists (groups of max(2, 8192 // k) lists per
+    workgroup): every level reads its input lists and writes its output
+    lists, the last one the indices."""
+    n = -(-((s.q_pos0 + s.Lq) // s.m) // fused_cols(s.topk))
+    g = max(2, 8192 // s.topk)
+    total = 0
+    while True:
+        nout = -(-n // g)
+        total += s.B * s.Lq * n * s.topk * 8 + (s.B * s.Lq * nout * s.topk * 8 if nout > 1 else 0)
+        n = nout
+        if n <= 1:
+            break
+    return total + s.B * s.Lq * s.topk * 4
 
 
 def topk_bytes(s):
@@ -376,7 +391,7 @@ def bench_state_decode(args, torch, csa, wl, dev):
     # sequence, q_I and head weights, the candidate lists written and read,
     # the indices written
     vis = [(p + 1) // s.m for p in pos_l]
-    nch = (max(vis) + 2047) // 2048
+    nch = -(-max(vis) // fused_cols(s.topk))
     row = idx_row_bytes(s)
     ib = sum(vis) * row + s.B * s.H_I * (row + 4) + 2 * s.B * nch * s.topk * 8 + s.B * s.topk * 4
     roof = {"bound": "hbm", "achieved": ib / (breakdown["index_topk"] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
@@ -1176,16 +1191,18 @@ def main():
         step_bytes = dom_bytes
     elif W == "pair_1m":
         metric, unit = "CSA+HCA layer-pair decode query-tok/s @1M ctx", "query-tok/s"
-        dom = "csa.index_qk"
-        dom_bytes = index_qk_bytes(main_shape)
+        # the CSA half's indexer runs fused (k = 1024: 4096-entry chunks)
+        dom = "csa.index_cand" if fused(main_shape) else "csa.index_qk"
+        dom_bytes = index_cand_bytes(main_shape) if fused(main_shape) else index_qk_bytes(main_shape)
         roof = {"bound": "hbm", "achieved": dom_bytes / (breakdown[dom] * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
         cfg = {"workload": "csa_hca_pair_1m_b8", "batch": main_shape.B, "context": main_shape.q_pos0 + 1,
                "csa_entries": main_shape.N_cap, "hca_entries": wl.CFG5_HCA.N_cap,
                "indexer": "%dx%d mxfp4" % (main_shape.H_I, main_shape.d_I), "topk": main_shape.topk,
                "heads": main_shape.H, "head_dim": main_shape.D, "window": main_shape.W}
-        step_bytes = (index_qk_bytes(main_shape) + topk_bytes(main_shape) + sparse_attn_bytes(main_shape)
-                      + hca_bytes(wl.CFG5_HCA))
+        sel_bytes = (index_cand_bytes(main_shape) + topk_merge_bytes(main_shape) if fused(main_shape)
+                     else index_qk_bytes(main_shape) + topk_bytes(main_shape))
+        step_bytes = sel_bytes + sparse_attn_bytes(main_shape) + hca_bytes(wl.CFG5_HCA)
     else:
         metric, unit = "indexer fp8 prefill query-tok/s @64K ctx", "query-tok/s"
         dom = "index_qk"

@@ -148,9 +148,10 @@ int csa_compress(int B, int T, int D, int m, int64_t pos0, int kv_dtype,
  *                  themselves are what csa_index_scores returns).
  *
  * When every indexer workgroup scores a single query (H_i >= 64, or Lq = 1)
- * and 4*topk <= 2048, the top-k runs fused: each workgroup keeps the top k of
- * its 2048-entry chunk in LDS and only those candidates reach HBM, to be
- * merged per query; the result is the same.
+ * and topk <= 1024, the top-k runs fused: each workgroup keeps the top k of
+ * its chunk of C entries in LDS (C = 2048 for topk <= 512, 4096 for
+ * topk <= 1024, so at most a quarter of the scores leave the chip) and only
+ * those candidates reach HBM, to be merged per query; the result is the same.
  */
 size_t csa_index_topk_ws_bytes(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, int topk);
 int csa_index_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap,
@@ -191,13 +192,14 @@ int csa_topk(int B, int Lq, int64_t q_pos0, int m, int64_t N_cap, const float* s
  * csa_index_topk returns.
  *
  * csa_index_candidates: the indexer of csa_index_topk with the top k of each
- * 2048-entry chunk of a row kept on chip. For every query row (b, i) and
- * chunk c < ceil(n(q_pos0+Lq-1) / 2048) it writes a list of topk pairs: keys
+ * chunk of C entries of a row kept on chip (C = 2048 for topk <= 512, 4096
+ * for topk <= 1024). For every query row (b, i) and chunk
+ * c < nc = ceil(n(q_pos0+Lq-1) / C) it writes a list of topk pairs: keys
  * (uint32, order-preserving images of the scores: a larger score has a
  * larger key, -0 and +0 share one) at cand[(((b*Lq + i) * nc + c) * topk]
  * and the entry indices at the same offset past the rows * nc * topk keys,
  * in ascending index, padded with key 0 / index -1. Arguments and limits of
- * csa_index_topk, plus H_i >= 64 or Lq == 1, and 4*topk <= 2048
+ * csa_index_topk, plus H_i >= 64 or Lq == 1, and topk <= 1024
  * (else CSA_ERR_SHAPE).
  * csa_topk_merge: the top k of each row's lists by (key descending, index
  * ascending) into idx_out [B, Lq, topk] int32, ascending index, -1 padding.

@@ -116,16 +116,17 @@ int csa_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t* po
              ? CSA_ERR_LAUNCH : CSA_OK;
 }
 
-// Fused indexer + per-chunk top-k: candidate lists of the chunks of kIdxColsPerWG
-// entries, merged by the top-k merge levels.
+// Fused indexer + per-chunk top-k: candidate lists of the chunks of
+// index_fused_cols(k) entries, merged by the top-k merge levels.
 static size_t fused_bytes(int B, int Lq, int64_t q_pos0, int m, int topk) {
-  return topk_merge_ws_bytes((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk);
+  return topk_merge_ws_bytes((int64_t)B * Lq, index_fused_nchunks(q_pos0, Lq, m, topk), topk);
 }
 
 // The indexer's top-k runs fused when every indexer workgroup scores one query
-// (H_i >= 64, or a single query row) and k keeps at most a quarter of a chunk.
+// (H_i >= 64, or a single query row) and k <= 1024 (a chunk of at least 4k
+// entries).
 static bool use_fused(int Lq, int H_i, int topk) {
-  return (index_qk_queries_per_group(H_i) == 1 || Lq == 1) && 4 * topk <= index_qk_list_len();
+  return (index_qk_queries_per_group(H_i) == 1 || Lq == 1) && index_fused_cols(topk) > 0;
 }
 
 static int launch_candidates(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
@@ -134,7 +135,7 @@ static int launch_candidates(int B, int Lq, int64_t q_pos0, const int64_t* q_pos
                              hipStream_t st) {
   const int64_t rows = (int64_t)B * Lq;
   uint32_t* ck = (uint32_t*)cand;
-  int32_t* ci = (int32_t*)(ck + rows * index_qk_nchunks(q_pos0, Lq, m) * topk);
+  int32_t* ci = (int32_t*)(ck + rows * index_fused_nchunks(q_pos0, Lq, m, topk) * topk);
   return launch_index_qk_fused(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                                k_i_scale, topk, sbf, ck, ci, st);
 }
@@ -212,7 +213,7 @@ static int index_topk(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m
     if (launch_candidates(B, Lq, q_pos0, q_pos, m, N_cap, H_i, d_i, idx_dtype, q_i, q_i_scale, w_i, k_i,
                           k_i_scale, topk, sbf, ws, st))
       return CSA_ERR_LAUNCH;
-    return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, ws, idx_out, st)
+    return launch_topk_merge((int64_t)B * Lq, index_fused_nchunks(q_pos0, Lq, m, topk), topk, ws, idx_out, st)
                ? CSA_ERR_LAUNCH : CSA_OK;
   }
   float* scores = (float*)ws;
@@ -285,11 +286,11 @@ int csa_topk_merge(int B, int Lq, int64_t q_pos0, int m, int topk, void* cand, s
                    int32_t* idx_out, void* stream) {
   if (!cand || !idx_out) return CSA_ERR_NULL;
   if (B < 0 || Lq < 0 || q_pos0 < 0 || m < 1 || topk < 1 || topk > 2048) return CSA_ERR_SHAPE;
-  if (4 * topk > index_qk_list_len()) return CSA_ERR_SHAPE;
+  if (index_fused_cols(topk) == 0) return CSA_ERR_SHAPE;
   if (!aligned16(cand) || !aligned16(idx_out)) return CSA_ERR_ALIGN;
   if (cand_bytes < csa_index_candidates_bytes(B, Lq, q_pos0, m, topk)) return CSA_ERR_WORKSPACE;
   if ((int64_t)B * Lq == 0) return CSA_OK;
-  return launch_topk_merge((int64_t)B * Lq, index_qk_nchunks(q_pos0, Lq, m), topk, cand, idx_out,
+  return launch_topk_merge((int64_t)B * Lq, index_fused_nchunks(q_pos0, Lq, m, topk), topk, cand, idx_out,
                            as_stream(stream)) ? CSA_ERR_LAUNCH : CSA_OK;
 }
 

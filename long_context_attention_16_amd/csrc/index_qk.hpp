@@ -28,8 +28,8 @@
 namespace csa {
 
 constexpr int kIdxWaves = 4;
-constexpr int kIdxTilesPerWave = 16;
-constexpr int kIdxColsPerWG = kIdxWaves * kIdxTilesPerWave * 32;  // entries per workgroup
+constexpr int kIdxTilesPerWave = 16;  // 32-entry tiles per wave: scores to HBM, and fused with k <= 512
+constexpr int kIdxColsPerWG = kIdxWaves * kIdxTilesPerWave * 32;  // entries per workgroup (2048)
 
 // Operand fragment of one MFMA k-step for one lane, by format. The order in
 // which the d_I elements of a row are fed to the k-steps is free as long as
@@ -121,7 +121,7 @@ template <> struct IdxOp<3> {  // MXFP4: 32 e2m1 codes (16 bytes) at 64s + 32*ha
 template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() { return 2; }
 
 // Scores for one group of queries (MTILES*32 rows = G queries x HI heads)
-// against the kIdxColsPerWG entries of chunk c. Wave w takes the 32-entry
+// against the kIdxWaves * TPW * 32 entries of chunk c. Wave w takes the 32-entry
 // tiles w, w + 4, w + 8, ... of the chunk; its trip count nt is wave-uniform.
 // Tiles stream through a ring of NBUF register buffers: the loads of tile
 // i + NBUF - 1 are issued before tile i is multiplied, so up to NBUF - 1
@@ -137,18 +137,22 @@ template <int FMT, int MTILES, int DI> constexpr int idx_nbuf() { return 2; }
 // candidate list of k (key, index) pairs per (row, chunk) in ascending index
 // order, padded with key 0 / index -1. The lists of a row are merged by the
 // top-k merge kernel; every entry of the row's top k is in its chunk's top k.
+// A fused chunk holds at least 4k entries (TPW = 16 tiles per wave, 2048
+// entries, for k <= 512; 32 tiles, 4096 entries, for k <= 1024), so the lists
+// carry at most a quarter of the scores.
 // LDS of one indexer workgroup (a struct, so that a kernel running several
 // kinds of work can overlay it with the others' in one buffer).
-template <int FMT, int HI, int DI, bool FUSE> struct IdxShared {
+template <int FMT, int HI, int DI, bool FUSE, int TPW> struct IdxShared {
+  static constexpr int COLS = kIdxWaves * TPW * 32;  // entries per chunk
   static constexpr int MTILES = HI == 128 ? 4 : 2;
   static constexpr int G = MTILES * 32 / HI;  // queries per group
   typedef IdxOp<FMT> Op;
   typedef typename Op::Frag Frag;
   static constexpr int KS = (DI + Op::KW - 1) / Op::KW;
   static constexpr int kSelThreads = kIdxWaves * kWave;
-  static constexpr int kSelKPT = kIdxColsPerWG / kSelThreads;
+  static constexpr int kSelKPT = COLS / kSelThreads;
   typedef TopkShared<kSelThreads, kSelKPT> SelShared;
-  static constexpr int kScBytes = (kIdxColsPerWG + kWave) * 4;
+  static constexpr int kScBytes = (COLS + kWave) * 4;
   int s_lim[G];                         // per query: visible entries n(t)
   float4 s_w[MTILES * 8];               // head weight of each of the MTILES*32 rows
   Frag s_a[MTILES * KS * kWave];        // q operand fragments
@@ -159,20 +163,21 @@ template <int FMT, int HI, int DI, bool FUSE> struct IdxShared {
 };
 
 // One indexer work unit: blk is the unit's index (a kernel's block index).
-template <int FMT, int HI, int DI, bool FUSE>
+template <int FMT, int HI, int DI, bool FUSE, int TPW>
 __device__ __forceinline__ void index_qk_body(
-    IdxShared<FMT, HI, DI, FUSE>& S, const int blk,
+    IdxShared<FMT, HI, DI, FUSE, TPW>& S, const int blk,
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
     const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores, int sbf,
     int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
-  typedef IdxShared<FMT, HI, DI, FUSE> Sh;
+  typedef IdxShared<FMT, HI, DI, FUSE, TPW> Sh;
+  constexpr int COLS = Sh::COLS;
   constexpr int MTILES = Sh::MTILES;
   constexpr int G = Sh::G;
   constexpr int NBUF = idx_nbuf<FMT, MTILES, DI>();
   // Padded steps of the ring then only ever fall on tiles past the group's
   // visible entries (stores masked), never past the end of the chunk.
-  static_assert(kIdxTilesPerWave % NBUF == 0, "ring depth divides the tiles per wave");
+  static_assert(TPW % NBUF == 0, "ring depth divides the tiles per wave");
   constexpr int kSelThreads = Sh::kSelThreads;
   constexpr int kSelKPT = Sh::kSelKPT;
   typedef IdxOp<FMT> Op;
@@ -194,7 +199,7 @@ __device__ __forceinline__ void index_qk_body(
   const int lane = threadIdx.x % kWave;
   const int half = lane / 32;
   const int l32 = lane % 32;
-  const int c = blk % nchunks;  // chunk of kIdxColsPerWG entries
+  const int c = blk % nchunks;  // chunk of COLS entries
   const int gg = blk / nchunks;
   const int b = gg / ngroups;
   q_pos0 = seq_pos(q_pos, q_pos0, b);  // from here on: this sequence's row-0 position
@@ -202,7 +207,7 @@ __device__ __forceinline__ void index_qk_body(
   const int nq = min(G, Lq - i0);
   const int64_t n_last = (q_pos0 + i0 + nq) / m;  // visible entries of the group's last query
   const int ntiles = (int)((n_last + 31) / 32);   // 32-entry tiles holding any of them
-  const int tile0 = c * kIdxWaves * kIdxTilesPerWave;
+  const int tile0 = c * kIdxWaves * TPW;
   auto tile_of = [&](int i) { return tile0 + kIdxWaves * i + wave; };
   if (tile0 >= ntiles) {
     if constexpr (FUSE) {  // an empty chunk: a padding list
@@ -215,7 +220,7 @@ __device__ __forceinline__ void index_qk_body(
     return;
   }
   const int nt = tile0 + wave < ntiles
-                     ? min(kIdxTilesPerWave, (ntiles - tile0 - wave + kIdxWaves - 1) / kIdxWaves) : 0;
+                     ? min(TPW, (ntiles - tile0 - wave + kIdxWaves - 1) / kIdxWaves) : 0;
   const int tmax = max(nt - 1, 0);
 
   const int64_t kbase = (int64_t)b * N_cap;
@@ -287,7 +292,7 @@ __device__ __forceinline__ void index_qk_body(
   const int col0 = tile0 * 32;
   auto put = [&](int qq, int jrel, bool ok, float v) {
     if constexpr (FUSE) {
-      s_sc[ok ? jrel - col0 : kIdxColsPerWG + lane] = v;  // one query: qq == 0 whenever ok
+      s_sc[ok ? jrel - col0 : COLS + lane] = v;  // one query: qq == 0 whenever ok
     } else {
       const uint32_t word = score_word(v, sbf);
       const int off = ok && s_lane ? (int)((uint32_t)qq * srow + (uint32_t)jrel * (uint32_t)esz) : kDrop;
@@ -385,7 +390,7 @@ __device__ __forceinline__ void index_qk_body(
 
   if constexpr (FUSE) {
     __syncthreads();  // the chunk's scores are in s_sc
-    const int n = (int)max<int64_t>(0, min<int64_t>(kIdxColsPerWG, (int64_t)s_lim[0] - col0));
+    const int n = (int)max<int64_t>(0, min<int64_t>(COLS, (int64_t)s_lim[0] - col0));
     const int64_t o = (((int64_t)b * Lq + i0) * nchunks + c) * topk;
     uint32_t* ok = cand_key + o;
     int32_t* oi = cand_idx + o;
@@ -415,14 +420,14 @@ __device__ __forceinline__ void index_qk_body(
   }
 }
 
-template <int FMT, int HI, int DI, bool FUSE>
+template <int FMT, int HI, int DI, bool FUSE, int TPW>
 __global__ __launch_bounds__(kIdxWaves * kWave) void index_qk_kernel(
     int Lq, int64_t q_pos0, const int64_t* __restrict__ q_pos, int m, int64_t N_cap, int ngroups, int nchunks,
     const uint8_t* __restrict__ q_i, const uint8_t* __restrict__ q_s, const float* __restrict__ w_i,
     const uint8_t* __restrict__ k_i, const uint8_t* __restrict__ k_s, float* __restrict__ scores, int sbf,
     int topk, uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
-  __shared__ IdxShared<FMT, HI, DI, FUSE> S;
-  index_qk_body<FMT, HI, DI, FUSE>(S, blockIdx.x, Lq, q_pos0, q_pos, m, N_cap, ngroups, nchunks, q_i, q_s, w_i, k_i,
+  __shared__ IdxShared<FMT, HI, DI, FUSE, TPW> S;
+  index_qk_body<FMT, HI, DI, FUSE, TPW>(S, blockIdx.x, Lq, q_pos0, q_pos, m, N_cap, ngroups, nchunks, q_i, q_s, w_i, k_i,
                                    k_s, scores, sbf, topk, cand_key, cand_idx);
 }
 
@@ -446,19 +451,19 @@ struct IdxArgs {
   int32_t* ci;
 };
 
-template <int FMT, int HI, int DI, bool FUSE>
+template <int FMT, int HI, int DI, bool FUSE, int TPW>
 void idx_go(const IdxArgs& a) {
-  hipLaunchKernelGGL((index_qk_kernel<FMT, HI, DI, FUSE>), a.grid, dim3(kIdxWaves * kWave), 0, a.st, a.Lq,
+  hipLaunchKernelGGL((index_qk_kernel<FMT, HI, DI, FUSE, TPW>), a.grid, dim3(kIdxWaves * kWave), 0, a.st, a.Lq,
                      a.q_pos0, a.q_pos, a.m, a.N_cap, a.ngroups, a.nchunks, a.q, a.qs, a.w, a.k, a.ks, a.sc, a.sbf, a.topk,
                      a.ck, a.ci);
 }
 
-template <int FMT, bool FUSE>
+template <int FMT, bool FUSE, int TPW = kIdxTilesPerWave>
 void idx_dispatch(int H_i, int d_i, const IdxArgs& a) {
-#define CSA_IDX_D(HH)                                   \
-  if (d_i == 32) idx_go<FMT, HH, 32, FUSE>(a);          \
-  else if (d_i == 64) idx_go<FMT, HH, 64, FUSE>(a);     \
-  else idx_go<FMT, HH, 128, FUSE>(a)
+#define CSA_IDX_D(HH)                                        \
+  if (d_i == 32) idx_go<FMT, HH, 32, FUSE, TPW>(a);          \
+  else if (d_i == 64) idx_go<FMT, HH, 64, FUSE, TPW>(a);     \
+  else idx_go<FMT, HH, 128, FUSE, TPW>(a)
   switch (H_i) {
     case 4: CSA_IDX_D(4); break;
     case 8: CSA_IDX_D(8); break;
@@ -472,11 +477,11 @@ void idx_dispatch(int H_i, int d_i, const IdxArgs& a) {
 
 inline IdxArgs idx_args(int B, int Lq, int64_t q_pos0, const int64_t* q_pos, int m, int64_t N_cap, int H_i,
                         const void* q_i, const uint8_t* q_s, const float* w_i, const void* k_i,
-                        const uint8_t* k_s, hipStream_t stream) {
+                        const uint8_t* k_s, hipStream_t stream, int nchunks) {
   IdxArgs a{};
   const int G = index_qk_queries_per_group(H_i);
   a.ngroups = (Lq + G - 1) / G;
-  a.nchunks = index_qk_nchunks(q_pos0, Lq, m);
+  a.nchunks = nchunks;
   a.grid = dim3((unsigned)((int64_t)B * a.ngroups * a.nchunks));
   a.st = stream;
   a.Lq = Lq; a.q_pos0 = q_pos0; a.q_pos = q_pos; a.m = m; a.N_cap = N_cap;

@@ -80,10 +80,14 @@ int launch_state_append(int B, int D, int m, int R, int kv_dtype, const int64_t*
                         uint8_t* ki_c_scale, hipStream_t stream);
 // Query rows scored together by one indexer workgroup (64 / H_i, 1 for H_i = 128).
 int index_qk_queries_per_group(int H_i);
-// Entries per indexer workgroup (the length of a fused candidate source chunk)
-// and the number of such chunks per row.
-int index_qk_list_len();
+// Chunks of entries per row scored by the indexer workgroups when scores go
+// to HBM (2048 entries each).
 int index_qk_nchunks(int64_t q_pos0, int Lq, int m);
+// Fused indexer + chunk top-k: entries per chunk for top-k k (at least 4k:
+// 2048 for k <= 512, 4096 for k <= 1024; 0 = k too large to fuse) and the
+// chunks (candidate lists) per row.
+int index_fused_cols(int topk);
+int index_fused_nchunks(int64_t q_pos0, int Lq, int m, int topk);
 // Many-query fp8 indexer (64 heads of dim 128, at least 16 query rows per
 // sequence): same scores as launch_index_qk.
 bool index_qk_prefill_eligible(int fmt, int H_i, int d_i, int Lq);

@@ -112,8 +112,13 @@ static int kpt_for(int64_t n) { return n <= 4096 ? 4 : n <= 8192 ? 8 : n <= 1638
 
 static int topk_nchunks(int64_t n_max) { return (int)((n_max + kTkKeys - 1) / kTkKeys); }
 
-// Lists merged per workgroup at each level: as many as fit in 32768 keys.
-static int topk_group(int topk) { return max(2, kTkKeys / topk); }
+// Lists merged per workgroup at each level: as many as fit in 8192 keys (at
+// least two). A workgroup's select time grows with its keys, so many small
+// merges in parallel beat a few large ones: k = 1024 over 64 lists takes two
+// levels of 8192-key merges rather than 32768-key ones. The grouping cannot
+// change the result: every group keeps its own top k, and (-score, j) is a
+// total order, so the final level selects the row's exact top k.
+static int topk_group(int topk) { return max(2, 8192 / topk); }
 
 size_t topk_merge_ws_bytes(int64_t rows, int nlists, int topk) {
   if (nlists <= 1) return (size_t)rows * nlists * topk * 8;

@@ -60,6 +60,8 @@ def test_ws_queries(lib):
     assert lib.hca_dense_attn_ws_bytes(16, 1, 1048575, 128, 64, 512, 128) > 0
     # fused decode lists: 16 chunks of 2048 per row, k = 512, plus one merged list per row
     assert lib.csa_index_candidates_bytes(32, 1, 131071, 4, 512) == 32 * 512 * 8 * (16 + 1)
+    # k = 1024 at 1M: 64 chunks of 4096 per row, merged 8 lists at a time (8 level-1 lists)
+    assert lib.csa_index_candidates_bytes(8, 1, (1 << 20) - 1, 4, 1024) == 8 * 1024 * 8 * (64 + 8)
     # and csa_index_topk's workspace covers both of its paths
     assert lib.csa_index_topk_ws_bytes(32, 1, 131071, 4, 32768, 512) >= 32 * 512 * 8 * (16 + 1)
 
@@ -120,15 +122,16 @@ def test_index_topk_rejects(lib):
     cb = [1, 4, 200, 4, 64, 64, 128, 1, P, None, P, P, None, 8, P, nc, None]
     bad = list(cb); bad[5] = 32
     assert c(*bad) == SHAPE                       # 32 heads, 4 query rows: no fused path
-    bad = list(cb); bad[13] = 600
-    assert c(*bad) == SHAPE                       # k above a quarter of a 2048-entry chunk
+    bad = list(cb); bad[13] = 1100
+    assert c(*bad) == SHAPE                       # k above 1024: no fused path
     bad = list(cb); bad[15] = nc - 4
     assert c(*bad) == WS
     bad = list(cb); bad[14] = None
     assert c(*bad) == NULL
     mg = lib.csa_topk_merge
     assert mg(1, 4, 200, 4, 8, P, nc, None, None) == NULL
-    assert mg(1, 4, 200, 4, 600, P, nc, P, None) == SHAPE
+    assert mg(1, 4, 200, 4, 1100, P, nc, P, None) == SHAPE
+    assert mg(1, 4, 200, 4, 600, P, nc, P, None) == WS   # fused at k = 600: lists of 4096-entry chunks
     assert mg(1, 4, 200, 4, 8, P, nc - 4, P, None) == WS
     g = lib.csa_index_scores
     sb = [1, 4, 200, 4, 64, 4, 32, 1, P, None, P, P, None, P, None]

@@ -27,7 +27,8 @@ def _slice(t, b):
 
 @pytest.mark.parametrize("fmt,H_i,d_i,Lq,q_pos0,topk,score", [
     ("bf16", 64, 128, 1, 4 * 9000 - 1, 512, "f32"),     # fused: 5 chunks of 2048 and the merge
-    ("fp4", 64, 128, 1, 4 * 70000 - 1, 1024, "f32"),    # score path with chunked top-k and merge levels
+    ("fp4", 64, 128, 1, 4 * 70000 - 1, 1024, "f32"),    # fused: 18 chunks of 4096, two merge levels
+    ("fp4", 64, 128, 1, 4 * 70000 - 1, 2048, "f32"),    # k above 1024: score path, chunked top-k and merge
     ("fp8", 4, 32, 37, 20000, 300, "f32"),              # many query rows, the score path
     ("fp8", 64, 128, 20, 20000, 256, "bf16"),           # the many-query fp8 kernel, bf16 scores
     ("bf16", 64, 128, 1, 4 * 9000 - 1, 512, "bf16"),    # fused, bf16 scores

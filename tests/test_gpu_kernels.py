@@ -151,7 +151,7 @@ def _index_exact_case(fmt, H_i, d_i, B, Lq, q_pos0, m, N_cap, topk, seed):
     assert np.all(np.isneginf(got[~vis])), "invisible entries written"
     want_idx = otopk.topk_batch(want, topk, q_pos0, m)
     assert np.array_equal(idx.cpu().numpy(), want_idx), "top-k indices differ"
-    if (H_i >= 64 or Lq == 1) and 4 * topk <= 2048:
+    if (H_i >= 64 or Lq == 1) and topk <= 1024:
         # the fused path's two launches, called alone, give the same indices
         cand = csa.index_candidates(x["q_i"], x["w_i"], x["k_i"], topk, q_pos0, m, fmt,
                                     x["q_i_scale"], x["k_i_scale"])
@@ -184,6 +184,28 @@ def test_index_topk_fused_edges(n, topk):
     B, Lq, m = 2, 1, 4
     q_pos0 = 4 * n - 1
     _index_exact_case("bf16", 64, 128, B, Lq, q_pos0, m, n + 40, topk, seed=n + topk)
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "fp8", "fp4"])
+def test_index_topk_fused_k1024_exact(fmt):
+    # 512 < k <= 1024 runs fused over 4096-entry chunks: 4 chunks, the last
+    # one (712 entries) shorter than k, so its list is padded
+    B, Lq, m, topk = 2, 1, 4, 1024
+    n = 13000
+    _index_exact_case(fmt, 64, 128, B, Lq, 4 * n - 1, m, n + 5, topk, seed=31)
+
+
+@pytest.mark.parametrize("n,topk", [
+    (4096, 1024),     # one full chunk, n > k: the chunk select
+    (4097, 1024),     # a second chunk of one entry
+    (1000, 1024),     # n <= k: every entry, then -1 padding
+    (9000, 513),      # just above 512: 4096-entry chunks
+    (70000, 1024),    # 18 lists: two merge levels (8 lists per workgroup)
+    (300000, 1024),   # 74 lists: three merge levels
+])
+def test_index_topk_fused_k1024_edges(n, topk):
+    B, Lq, m = 2, 1, 4
+    _index_exact_case("fp4", 64, 128, B, Lq, 4 * n - 1, m, n + 40, topk, seed=n % 1000 + topk)
 
 
 @pytest.mark.parametrize("B,Lq,m,q_pos0,n_extra,topk", [
