@@ -1218,6 +1218,7 @@ def main():
     roof["traffic"] = measured_traffic(W, dom)
     roof["kernel"] = dom
     roof["bytes_per_launch"] = dom_bytes
+    roof["scope"] = "dominant kernel only (the whole step: step_hbm_gbs, step_frac)"
     roof = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()}
 
     result = {
@@ -1230,6 +1231,7 @@ def main():
         "timing": "value/ms_per_step: HIP-graph replays of the whole step; breakdown_us and roofline: "
                   "back-to-back launches of each call between HIP events",
         "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
+        "step_frac": round(step_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "copy_ceiling_gbs": copy_ceiling(torch, dev),
     }
     if W == "csa_decode":

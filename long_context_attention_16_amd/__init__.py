@@ -108,7 +108,10 @@ def _kv_dtype(t):
 
 
 def _ws(nbytes, device):
-    return torch.zeros((max(16, int(nbytes)) + 15) // 16 * 4, dtype=torch.float32, device=device)
+    """A workspace for a call made without one (the library needs no initial
+    contents, so none are written). Callers in a loop or under graph capture
+    pass their own `ws` and allocate nothing per call."""
+    return torch.empty((max(16, int(nbytes)) + 15) // 16 * 4, dtype=torch.float32, device=device)
 
 
 _IDX_ESIZE = {"f32": 4, "bf16": 2, "fp8": 1, "fp4": 1}
