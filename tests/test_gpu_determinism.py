@@ -56,7 +56,12 @@ def test_index_topk_deterministic_and_batch_invariant(fmt, H_i, d_i, Lq, q_pos0,
                        sb.view(torch.int16) if score == "bf16" else sb.view(torch.int32))
 
 
-@pytest.mark.parametrize("B,H,D,m,q_pos0,W", [(4, 64, 512, 128, 300000, 128), (3, 4, 128, 4, 5000, 16)])
+@pytest.mark.parametrize("B,H,D,m,q_pos0,W", [
+    (4, 64, 512, 128, 300000, 128),
+    (3, 4, 128, 4, 5000, 16),
+    # 1M context, 16 splits per row, a batch of 40 against a sequence alone
+    (40, 64, 512, 128, 1048575, 128),
+])
 def test_hca_deterministic_and_batch_invariant(B, H, D, m, q_pos0, W):
     g = _gen(B + H + m)
     N_cap = (q_pos0 + 1) // m + 1
