@@ -16,9 +16,9 @@
 //  * phase A, one workgroup per (query, chunk of 64 source rows), gathers the
 //    chunk's K rows into LDS, computes the logits of all H heads on MFMA and
 //    writes P' = 2^(l - m_c) in bf16 with the chunk's (m_c, sum P') per head;
-//  * phase B, one workgroup per (query, 64-wide slice of D), folds the chunk
-//    statistics and the sink into per-chunk factors 2^(m_c - M) / den,
-//    gathers the V slices of all rows (128 contiguous bytes each) and
+//  * phase B, one workgroup per (query, slice of 64 dims, or of 32 when a
+//    call has few query rows), folds the chunk statistics and the sink into
+//    per-chunk factors 2^(m_c - M) / den, gathers the V slices of all rows and
 //    accumulates O = sum_r P_r V_r on MFMA, already normalized.
 // P' carries no more rounding than the PV product needs anyway (P enters the
 // MFMA in bf16). Every reduction runs in a fixed order, so results are
@@ -42,14 +42,26 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int
   dec_a_body<NW>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
 }
 
-template <int NW>
+template <int NW, int DSL>
 __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int nchunk, int spad,
                                                                   const uint16_t* __restrict__ pp,
                                                                   const float* __restrict__ ml,
                                                                   const int64_t* __restrict__ rowsrc) {
-  __shared__ DecBShared<NW, kBrowsMax> L;
-  const int rows = gridDim.x / kNsl;
-  dec_b_body<NW, kBrowsMax>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
+  __shared__ DecBShared<NW, kBrowsMax, DSL> L;
+  const int rows = gridDim.x / (kDecD / DSL);
+  dec_b_body<NW, kBrowsMax, DSL>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
 }
 
 }  // namespace
@@ -60,7 +72,6 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
 using dec::kDecD;
 using dec::kArows;
 using dec::kMaxChunks;
-using dec::kNsl;
 
 bool attn_decode_eligible(int kv_dtype, bool hca, int H, int D, int topk, int W) {
   return !hca && kv_dtype == 1 && D == kDecD && H % 16 == 0 && H >= 16 && H <= 128 && topk + W > 0 &&
@@ -86,11 +97,17 @@ int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
   float* ml = (float*)((char*)ws + ((size_t)rows * a.H * spad * 2 + 255) / 256 * 256);
   int64_t* rowsrc = (int64_t*)((char*)ml + ((size_t)rows * nc * a.H * 8 + 255) / 256 * 256);
   if (nc == 0) return 1;
-#define CSA_DEC(NW)                                                                                       \
-  hipLaunchKernelGGL(attn_dec_qk_kernel<NW>, dim3((unsigned)(rows * nc)), dim3(NW * kWave), 0, st, a, nc,  \
-                     spad, pp, ml, rowsrc);                                                               \
-  hipLaunchKernelGGL(attn_dec_pv_kernel<NW>, dim3((unsigned)(rows * kNsl)), dim3(NW * kWave), 0, st, a, nc, \
-                     spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc)
+  // phase B: 64-dim slices when 8 per query row fill the chip, else 32
+  const bool wide = rows * (kDecD / 64) >= device_cus();
+#define CSA_DEC(NW)                                                                                           \
+  hipLaunchKernelGGL(attn_dec_qk_kernel<NW>, dim3((unsigned)(rows * nc)), dim3(NW * kWave), 0, st, a, nc,      \
+                     spad, pp, ml, rowsrc);                                                                   \
+  if (wide)                                                                                                   \
+    hipLaunchKernelGGL((attn_dec_pv_kernel<NW, 64>), dim3((unsigned)(rows * (kDecD / 64))), dim3(NW * kWave), \
+                       0, st, a, nc, spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc);    \
+  else                                                                                                        \
+    hipLaunchKernelGGL((attn_dec_pv_kernel<NW, 32>), dim3((unsigned)(rows * (kDecD / 32))), dim3(NW * kWave), \
+                       0, st, a, nc, spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc)
   switch (a.H / 16) {
     case 1: CSA_DEC(1); break;
     case 2: CSA_DEC(2); break;

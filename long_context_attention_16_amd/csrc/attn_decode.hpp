@@ -1,7 +1,7 @@
 // Device code of the two-launch CSA attention for many heads (one shared KV
 // head of dim 512 in bf16, H a multiple of 16): phase A (logits of all heads
 // against a chunk of 64 source rows) and phase B (P V over all rows for one
-// 64-wide slice of D), as work-unit bodies with their LDS in structs (a
+// 64- or 32-wide slice of D), as work-unit bodies with their LDS in structs (a
 // kernel can then overlay them with other work in one LDS buffer).
 //
 // Source: "DeepSeek V4 重磅開源！…" (InfoQ), section 混合注意力機制 (the
@@ -20,8 +20,6 @@ constexpr int kAtiles = kArows / 16;   // 16-row MFMA tiles of a chunk
 constexpr int kCtiles = kArows / 32;   // 32-row phase-B tiles of a chunk
 constexpr int kAline = 1024 + 16;    // LDS bytes per K row: 260 words, 4 mod 32, so the 16-byte fragment
                                      // reads of 8 consecutive rows hit 8 disjoint groups of 4 banks
-constexpr int kDsl = 64;             // D slice of a phase-B workgroup
-constexpr int kNsl = kDecD / kDsl;   // 8
 constexpr int kBrowsMax = 640;       // V rows staged at once by the standalone phase-B kernel
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLn2D = 0.6931471805599453f;
@@ -248,9 +246,14 @@ __device__ __forceinline__ void dec_a_body(DecAShared& L, const AttnArgs& p, con
 constexpr int kMaxChunks = (2048 + 256 + kArows - 1) / kArows;  // k <= 2048, W <= 256
 
 // LDS of a phase-B work unit staging BR rows at once.
-template <int NW, int BR> struct DecBShared {
+// Phase B's D slice: 64 dims (128 bytes of a row) when a call has enough
+// query rows to fill the chip with 8 slices each, else 32 (16 slices, twice
+// the workgroups). Each output element is the same MFMA sum either way (an
+// MFMA's sum for one element does not depend on the other elements of its
+// block), so the choice never changes a bit of the result.
+template <int NW, int BR, int DSL> struct DecBShared {
   static constexpr int H = 16 * NW;
-  __attribute__((aligned(16))) uint8_t Vs[BR * kDsl * 2];
+  __attribute__((aligned(16))) uint8_t Vs[BR * DSL * 2];
   float2 mls[kMaxChunks * H];
   const uint8_t* vsrc[BR];
   float fsc[BR / kArows][H];
@@ -258,8 +261,8 @@ template <int NW, int BR> struct DecBShared {
 };
 
 // Phase B of query row qrow, D slice sl, staging BR source rows at a time.
-template <int NW, int BR>
-__device__ __forceinline__ void dec_b_body(DecBShared<NW, BR>& L, const AttnArgs& p, const int qrow, const int sl,
+template <int NW, int BR, int DSL>
+__device__ __forceinline__ void dec_b_body(DecBShared<NW, BR, DSL>& L, const AttnArgs& p, const int qrow, const int sl,
                                            const int nchunk, const int spad, const uint16_t* __restrict__ pp,
                                            const float* __restrict__ ml, const int64_t* __restrict__ rowsrc) {
   constexpr int H = 16 * NW;
@@ -287,6 +290,9 @@ __device__ __forceinline__ void dec_b_body(DecBShared<NW, BR>& L, const AttnArgs
   // together, each consumed at once into LDS so none is deferred to a later
   // use.
   const int64_t* rs = rowsrc + (int64_t)qrow * spad;
+  constexpr int kDsl = DSL;
+  constexpr int RPC = 1024 / (kDsl * 2);  // rows per wave copy (16-byte lanes)
+  constexpr int CPR = kDsl * 2 / 16;      // 16-byte chunks per row slice
   const uint8_t* vbase = (const uint8_t*)p.v_c + sl * kDsl * 2;
   const uint8_t* rbase = (const uint8_t*)p.v_raw + sl * kDsl * 2;
   auto put_sources = [&](int rb, int nrows) {
@@ -297,21 +303,25 @@ __device__ __forceinline__ void dec_b_body(DecBShared<NW, BR>& L, const AttnArgs
     for (int it = 0; it < kSrcIt; ++it)
       if (tid + it * NT < nrows) vsrc[tid + it * NT] = e[it] >= 0 ? vbase + e[it] * 2 : rbase + (~e[it]) * 2;
   };
-  // V slices of a block into LDS: each wave copy moves 8 rows x 128 bytes.
-  // A 128-byte row spans every bank once, so the 16-byte chunks of row r
-  // are stored XOR-swizzled (position = chunk ^ 2 (r % 4)): lane l of the
-  // copy, which lands at chunk position l % 8 of row L*8 + l/8, fetches the
-  // global chunk that belongs there.
+  // V slices of a block into LDS: each wave copy moves RPC rows of 2*DSL
+  // bytes, stored XOR-swizzled so that the transposed reads below are
+  // conflict-free: 128-byte rows (one row spans every bank) take chunk
+  // position = chunk ^ 2 (r % 4); 64-byte rows (four rows share the banks,
+  // and a half-wave's reads would put rows r and r + 8 on the same banks)
+  // take chunk ^ 2 ((r / 8) % 2), which sends r + 8 to the other half.
+  // Lane l of the copy, which lands at chunk position l % CPR of row
+  // L*RPC + l/CPR, fetches the global chunk that belongs there.
   // A fixed trip count (rows past nrows re-copy the last row into slots
   // that are never read): a loop with a data-dependent count would make the
   // compiler drain every load in flight (the P' fragments) before it.
   auto copy_block = [&](int nrows) {
 #pragma unroll
-    for (int u = 0; u < (kBrows / 8 + NW - 1) / NW; ++u) {
+    for (int u = 0; u < (kBrows / RPC + NW - 1) / NW; ++u) {
       const int L_ = wave + NW * u;
-      if ((kBrows / 8) % NW != 0 && L_ >= kBrows / 8) break;  // wave-uniform
-      const int r = L_ * 8 + lane / 8;
-      __builtin_amdgcn_global_load_lds((const void*)(vsrc[min(r, nrows - 1)] + (((lane % 8) ^ (2 * (r % 4))) * 16)),
+      if ((kBrows / RPC) % NW != 0 && L_ >= kBrows / RPC) break;  // wave-uniform
+      const int r = L_ * RPC + lane / CPR;
+      const int swz = DSL == 64 ? 2 * (r % 4) : 2 * ((r / 8) % 2);
+      __builtin_amdgcn_global_load_lds((const void*)(vsrc[min(r, nrows - 1)] + (((lane % CPR) ^ swz) * 16)),
                                        (__attribute__((address_space(3))) void*)(Vs + L_ * 1024), 16, 0, 0);
     }
   };
@@ -401,9 +411,10 @@ __device__ __forceinline__ void dec_b_body(DecBShared<NW, BR>& L, const AttnArgs
         // V^T fragments by transposed LDS reads: lane (d = l16, g) gets rows
         // 8g..8g+7 of column 16*dt + l16. Lane j of a 16-lane group reads 8
         // bytes at row ra = 32t + 8g + j/4 (+4), columns 16 dt + 4 (j%4) ..+3:
-        // chunk 2 dt + (j%4)/2 of the row, swizzled as stored (ra % 4 = j/4).
+        // chunk 2 dt + (j%4)/2 of the row, swizzled as stored (ra % 4 = j/4;
+        // (ra / 8) % 2 = g % 2, also for ra + 4).
         const int ra = 32 * t + 8 * g + l16 / 4;
-        const int sw = 2 * (l16 / 4);
+        const int sw = DSL == 64 ? 2 * (l16 / 4) : 2 * (g % 2);
 #pragma unroll
         for (int dt = 0; dt < kDsl / 16; ++dt) {
           const int off = (((2 * dt + (l16 % 4) / 2) ^ sw) * 16) + (l16 % 2) * 8;
