@@ -32,6 +32,8 @@ def _gen(seed):
     ("bf16", 16, 128, 1, 7, 140000, 4, 700, False, 0),  # two chunk lists per row, merged
     ("fp8", 64, 128, 2, 20, 4001, 4, 64, False, 0),     # many-query fp8 kernel, odd N_cap
     ("fp8", 4, 32, 2, 3, 2001, 1, 50, True, 2),         # unfused, per-sequence positions
+    ("fp4", 64, 128, 2, 1, 4 * 13000 - 1, 4, 1024, False, 3),  # fused over 4096-entry chunks, 16-bit keys
+    ("bf16", 64, 128, 3, 1, 4 * 9000 - 1, 4, 600, True, 0),    # the same with per-sequence positions
 ])
 def test_index_topk_bf16_scores_exact(fmt, H_i, d_i, B, Lq, q_pos0, m, topk, varlen, extra):
     N_cap = (q_pos0 + Lq) // m + extra

@@ -154,6 +154,7 @@ def _exact_indexer(B, Lq, H_i, d_i, N_cap, fmt, seed):
     ("bf16", 64, 128, 1, 4, 512),    # the fused decode path
     ("fp8", 64, 128, 1, 4, 100),
     ("fp4", 64, 128, 1, 4, 64),
+    ("fp4", 64, 128, 1, 4, 1024),    # fused over 4096-entry chunks, rows of different lengths
     ("bf16", 4, 32, 3, 4, 50),       # grouped queries, scores + top-k
     ("fp8", 64, 128, 20, 4, 64),     # the many-query fp8 kernel
 ])
