@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int
 }
 
 // Compute units of the current device (cached per device).
-int device_cus() {
+static int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
