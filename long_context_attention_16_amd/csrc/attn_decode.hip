@@ -42,14 +42,14 @@ __global__ __launch_bounds__(NW * kWave) void attn_dec_qk_kernel(AttnArgs p, int
   dec_a_body<NW>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
 }
 
-template <int NW, int DSL>
+template <int NW, int DSL, int BR>
 __global__ __launch_bounds__(NW * kWave) void attn_dec_pv_kernel(AttnArgs p, int nchunk, int spad,
                                                                   const uint16_t* __restrict__ pp,
                                                                   const float* __restrict__ ml,
                                                                   const int64_t* __restrict__ rowsrc) {
-  __shared__ DecBShared<NW, kBrowsMax, DSL> L;
+  __shared__ DecBShared<NW, BR, DSL> L;
   const int rows = gridDim.x / (kDecD / DSL);
-  dec_b_body<NW, kBrowsMax, DSL>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
+  dec_b_body<NW, BR, DSL>(L, p, blockIdx.x % rows, blockIdx.x / rows, nchunk, spad, pp, ml, rowsrc);
 }
 
 // Compute units of the current device (cached per device).
@@ -97,17 +97,25 @@ int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
   float* ml = (float*)((char*)ws + ((size_t)rows * a.H * spad * 2 + 255) / 256 * 256);
   int64_t* rowsrc = (int64_t*)((char*)ml + ((size_t)rows * nc * a.H * 8 + 255) / 256 * 256);
   if (nc == 0) return 1;
-  // phase B: 64-dim slices when 8 per query row fill the chip, else 32
-  const bool wide = rows * (kDecD / 64) >= device_cus();
+  // phase B: 64-dim slices when 8 per query row fill the chip, else 32-dim
+  // slices (twice the workgroups); staging 640 rows at a time, or, when the
+  // 32-dim workgroups fit one per CU and a list is longer, 1152 (one block
+  // for k = 1024 and W = 128, in LDS that leaves room for one workgroup per CU)
+  const int cus = device_cus();
+  const int kind = rows * (kDecD / 64) >= cus ? 0 : spad > kBrowsMax && rows * (kDecD / 32) <= cus ? 2 : 1;
+#define CSA_DEC_B(NW, DSL, BR)                                                                                \
+  hipLaunchKernelGGL((attn_dec_pv_kernel<NW, DSL, BR>), dim3((unsigned)(rows * (kDecD / DSL))),               \
+                     dim3(NW * kWave), 0, st, a, nc, spad, (const uint16_t*)pp, (const float*)ml,            \
+                     (const int64_t*)rowsrc)
 #define CSA_DEC(NW)                                                                                           \
   hipLaunchKernelGGL(attn_dec_qk_kernel<NW>, dim3((unsigned)(rows * nc)), dim3(NW * kWave), 0, st, a, nc,      \
                      spad, pp, ml, rowsrc);                                                                   \
-  if (wide)                                                                                                   \
-    hipLaunchKernelGGL((attn_dec_pv_kernel<NW, 64>), dim3((unsigned)(rows * (kDecD / 64))), dim3(NW * kWave), \
-                       0, st, a, nc, spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc);    \
+  if (kind == 0)                                                                                              \
+    CSA_DEC_B(NW, 64, kBrowsMax);                                                                             \
+  else if (kind == 1)                                                                                         \
+    CSA_DEC_B(NW, 32, kBrowsMax);                                                                             \
   else                                                                                                        \
-    hipLaunchKernelGGL((attn_dec_pv_kernel<NW, 32>), dim3((unsigned)(rows * (kDecD / 32))), dim3(NW * kWave), \
-                       0, st, a, nc, spad, (const uint16_t*)pp, (const float*)ml, (const int64_t*)rowsrc)
+    CSA_DEC_B(NW, 32, kBrowsNarrow)
   switch (a.H / 16) {
     case 1: CSA_DEC(1); break;
     case 2: CSA_DEC(2); break;
@@ -119,6 +127,7 @@ int launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
     default: CSA_DEC(8); break;
   }
 #undef CSA_DEC
+#undef CSA_DEC_B
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

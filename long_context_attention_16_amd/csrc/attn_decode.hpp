@@ -20,7 +20,8 @@ constexpr int kAtiles = kArows / 16;   // 16-row MFMA tiles of a chunk
 constexpr int kCtiles = kArows / 32;   // 32-row phase-B tiles of a chunk
 constexpr int kAline = 1024 + 16;    // LDS bytes per K row: 260 words, 4 mod 32, so the 16-byte fragment
                                      // reads of 8 consecutive rows hit 8 disjoint groups of 4 banks
-constexpr int kBrowsMax = 640;       // V rows staged at once by the standalone phase-B kernel
+constexpr int kBrowsMax = 640;       // V rows staged at once by phase B
+constexpr int kBrowsNarrow = 1152;   // ... when its workgroups are few (one per CU)
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLn2D = 0.6931471805599453f;
 
