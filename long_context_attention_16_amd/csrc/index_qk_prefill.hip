@@ -228,42 +228,76 @@ __global__ __launch_bounds__(kPfWaves * kWave) void index_qk_prefill_kernel(
   // (past the last block the copy repeats it into a free buffer and the
   // fragment read is unused), so the compiler's own wait analysis sees the
   // same counts on every path and adds none.
-  i32x8 kf[2];
-  f32x16 acc[4];
-  auto block = [&](int blk, const uint8_t* kt, const uint8_t* kt_next) {
+  // The two waves of a SIMD (waves w and w + 4) run half a step apart: the
+  // second half of the waves does its block hand-over after the last
+  // epilogue instead of before it, so right after every barrier one wave of
+  // each pair runs an epilogue (VALU) while the other runs MFMAs, and the
+  // two stay in alternation through the block instead of contending for the
+  // same unit at the same time.
+  auto run = [&](auto late_c) {
+    constexpr bool late = decltype(late_c)::value;
+    i32x8 kf[2];
+    f32x16 acc[4];
+    auto handover = [&](int blk, const uint8_t* kt, const uint8_t* kt_next) {
+      __builtin_amdgcn_s_waitcnt(pf_vmcnt(kPfLoads + kPfStores));
+      pf_lds_barrier();  // block blk+1 is in LDS; every wave is done with block blk
+      issue(min(blk + 3, nblk - 1), const_cast<uint8_t*>(kt));
+      frags(kt_next, 0, kf);
+    };
+    auto block = [&](int blk, const uint8_t* kt, const uint8_t* kt_next) {
 #pragma unroll
-    for (int st = 0; st < kPfSteps; ++st) {
-      mma(kf, acc);
-      if (st + 1 < kPfSteps) {
-        frags(kt, st + 1, kf);
-      } else {
-        __builtin_amdgcn_s_waitcnt(pf_vmcnt(kPfLoads + kPfStores));
-        pf_lds_barrier();  // block blk+1 is in LDS; every wave is done with block blk
-        issue(min(blk + 3, nblk - 1), const_cast<uint8_t*>(kt));
-        frags(kt_next, 0, kf);
+      for (int st = 0; st < kPfSteps; ++st) {
+        mma(kf, acc);
+        if (st + 1 < kPfSteps)
+          frags(kt, st + 1, kf);
+        else if (!late)
+          handover(blk, kt, kt_next);
+        // Nothing crosses these points: the reads stay right behind the MFMAs
+        // (the scheduler would sink them to the end of the epilogue and expose
+        // their latency), and the next step's MFMAs stay behind this epilogue
+        // (hoisted above it they would need a second accumulator set).
+        __builtin_amdgcn_sched_barrier(0);
+        epi(acc, blk * kPfSteps + st);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // Nothing crosses these points: the reads stay right behind the MFMAs
-      // (the scheduler would sink them to the end of the epilogue and expose
-      // their latency), and the next step's MFMAs stay behind this epilogue
-      // (hoisted above it they would need a second accumulator set).
-      __builtin_amdgcn_sched_barrier(0);
-      epi(acc, blk * kPfSteps + st);
-      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    __builtin_amdgcn_s_waitcnt(0);
+    pf_lds_barrier();  // blocks 0 and 1 are in LDS
+    issue(min(2, nblk - 1), s_k2);
+    frags(s_k0, 0, kf);
+    if constexpr (!late) {
+      for (int blk = 0;;) {
+        block(blk, s_k0, s_k1);
+        if (++blk >= nblk) break;
+        block(blk, s_k1, s_k2);
+        if (++blk >= nblk) break;
+        block(blk, s_k2, s_k0);
+        if (++blk >= nblk) break;
+      }
+    } else {
+      // the hand-over of block blk - 1 opens block blk (the loop's back edge
+      // then follows an epilogue's store, as in the other order), and a last
+      // barrier matches the other waves' count
+      block(0, s_k0, s_k1);
+      for (int blk = 1; blk < nblk;) {
+        handover(blk - 1, s_k0, s_k1);
+        block(blk, s_k1, s_k2);
+        if (++blk >= nblk) break;
+        handover(blk - 1, s_k1, s_k2);
+        block(blk, s_k2, s_k0);
+        if (++blk >= nblk) break;
+        handover(blk - 1, s_k2, s_k0);
+        block(blk, s_k0, s_k1);
+        ++blk;
+      }
+      pf_lds_barrier();
     }
   };
-
-  __builtin_amdgcn_s_waitcnt(0);
-  pf_lds_barrier();  // blocks 0 and 1 are in LDS
-  issue(min(2, nblk - 1), s_k2);
-  frags(s_k0, 0, kf);
-  for (int blk = 0;;) {
-    block(blk, s_k0, s_k1);
-    if (++blk >= nblk) break;
-    block(blk, s_k1, s_k2);
-    if (++blk >= nblk) break;
-    block(blk, s_k2, s_k0);
-    if (++blk >= nblk) break;
-  }
+  if (wave < kPfWaves / 2)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
   __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
 }
 
