@@ -36,6 +36,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+# Seconds of back-to-back work before any timed region: after an idle spell
+# the GPU's clocks ramp up over the first few tens of milliseconds of load
+# (measured: the fp8 prefill indexer 580 -> 400 -> 360 us per launch over its
+# first 40 launches, then flat for seconds; the decode step 98.5 -> 94.4 us),
+# so a handful of warmup steps would time the ramp, not the kernels.
+SETTLE_S = 0.25
+SETTLE_NOTE = "after %.2f s of back-to-back work (clock ramp-up)" % SETTLE_S
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Call fn(k) back to back until `seconds` have passed (synchronizing
+    every 8 calls); returns the number of calls."""
+    t_end = time.perf_counter() + seconds
+    k = 0
+    while True:
+        for _ in range(8):
+            fn(k)
+            k += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() >= t_end:
+            return k
 
 
 def parse():
@@ -221,6 +242,7 @@ def bench_compress(args, torch, csa, dev):
                 csa.compress(k_raw, v_raw, w_gate, m, 0, k_c, v_c)
         g.replay()
         torch.cuda.synchronize()
+        settle(torch, lambda k: g.replay())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(5):
@@ -244,7 +266,7 @@ def bench_compress(args, torch, csa, dev):
         "config": {"workload": "compress_seq1m_d512_m4", "cases": {c[0]: {"tokens": c[1], "head_dim": c[2], "m": c[3]}
                                                                   for c in COMPRESS_CASES}},
         "roofline": roof, "cases": out,
-        "timing": "HIP-graph replays of back-to-back calls per case",
+        "timing": "HIP-graph replays of back-to-back calls per case, " + SETTLE_NOTE,
         "copy_ceiling_gbs": copy_ceiling(torch, dev), "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -362,6 +384,14 @@ def bench_state_decode(args, torch, csa, wl, dev):
         for l in labels:
             launch(l, sets[k % 2])
     torch.cuda.synchronize()
+    graphs = []
+    for k in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in labels:
+                launch(l, sets[k])
+        graphs.append(g)
+    settle(torch, lambda k: graphs[k % 2].replay())
     breakdown = {}
     for l in labels:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -371,13 +401,6 @@ def bench_state_decode(args, torch, csa, wl, dev):
         e1.record()
         torch.cuda.synchronize()
         breakdown[l] = round(1000.0 * e0.elapsed_time(e1) / args.steps, 2)
-    graphs = []
-    for k in range(2):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for l in labels:
-                launch(l, sets[k])
-        graphs.append(g)
     for k in range(args.warmup):
         graphs[k % 2].replay()
     torch.cuda.synchronize()
@@ -410,7 +433,7 @@ def bench_state_decode(args, torch, csa, wl, dev):
                    "indexer": "%dx%d %s" % (s.H_I, s.d_I, s.idx), "topk": s.topk, "window": s.W},
         "roofline": roof, "breakdown_us": breakdown,
         "timing": "value/ms_per_step: HIP-graph replays of the whole step; breakdown_us: back-to-back calls "
-                  "between HIP events",
+                  "between HIP events; " + SETTLE_NOTE,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -461,6 +484,7 @@ def bench_bf16_scores(args, torch, csa, wl, dev):
                 scores_only(xs[k % 2], prec)
         g.replay()
         torch.cuda.synchronize()
+        settle(torch, lambda k: g.replay())
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(5):
@@ -479,6 +503,7 @@ def bench_bf16_scores(args, torch, csa, wl, dev):
                 call(xs[k % 2], prec)
         g.replay()
         torch.cuda.synchronize()
+        settle(torch, lambda k: g.replay())
         n_rep = max(1, args.steps // reps)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -521,7 +546,7 @@ def bench_bf16_scores(args, torch, csa, wl, dev):
         "indexer_speedup_bf16_over_f32": round(us_idx["f32"] / us_idx["bf16"], 3),
         "indexer_scores_gbs": {p: round((base - s.B * s.Lq * s.topk * 4 + s.B * vis * (4 if p == "f32" else 2))
                                         / (v * 1e-6) / 1e9, 1) for p, v in us_idx.items()},
-        "timing": "HIP-graph replays of back-to-back calls, two input sets alternating",
+        "timing": "HIP-graph replays of back-to-back calls, two input sets alternating, " + SETTLE_NOTE,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -575,6 +600,13 @@ def bench_prefill(args, torch, csa, wl, dev):
     for k in range(max(args.warmup, 2)):
         step(k)
     torch.cuda.synchronize()
+    graphs = []
+    for k in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(k)
+        graphs.append(g)
+    settle(torch, lambda k: graphs[k % 2].replay())
     reps = max(4, min(args.steps, 20))
     breakdown = {}
     for name, f in calls.items():
@@ -585,12 +617,6 @@ def bench_prefill(args, torch, csa, wl, dev):
         e1.record()
         torch.cuda.synchronize()
         breakdown[name] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
-    graphs = []
-    for k in range(2):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(k)
-        graphs.append(g)
     for k in range(2):
         graphs[k].replay()
     torch.cuda.synchronize()
@@ -640,7 +666,7 @@ def bench_prefill(args, torch, csa, wl, dev):
                      "sparse_attn": round(roof["achieved"], 1)},
         "gather_gbs": round(gathered / t_attn / 1e9, 1),
         "timing": "value/ms_per_step: HIP-graph replays of the three calls; breakdown_us: back-to-back launches "
-                  "of each call between HIP events",
+                  "of each call between HIP events; " + SETTLE_NOTE,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -761,6 +787,7 @@ def bench_attn_bwd(args, torch, csa, wl, dev):
         for _ in range(2):
             call()
         torch.cuda.synchronize()
+        settle(torch, lambda k: call())
         reps = max(3, args.steps // 10)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -792,7 +819,7 @@ def bench_attn_bwd(args, torch, csa, wl, dev):
                    "heads": c[1].H, "head_dim": c[1].D, "topk": c[1].topk, "window": c[1].W, "kv": c[1].kv}
                    for c in cases}},
         "roofline": roof, "cases": res,
-        "timing": "HIP events over back-to-back calls",
+        "timing": "HIP events over back-to-back calls, " + SETTLE_NOTE,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -833,13 +860,14 @@ def _oracle_bwd_baseline(s, x, idx, dout, seconds):
                       % (done, s.Lq, spent)}
 
 
-def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10):
+def copy_ceiling(torch, dev, nbytes=1 << 30, reps=10, settle_s=SETTLE_S):
     """Read+write bandwidth of a plain device copy of nbytes (context for the
     roofline, and the calibration kernel for HBM byte counters)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)
     torch.cuda.synchronize()
+    settle(torch, lambda k: dst.copy_(src), settle_s)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -871,6 +899,7 @@ def prefill_indexer_mfma(torch, csa, wl, dev, reps=20, warmup=10):
                          out=x["scores"])
     for k in range(warmup):
         launch(xs[k % 2])
+    settle(torch, lambda k: launch(xs[k % 2]))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for k in range(reps):
@@ -884,7 +913,7 @@ def prefill_indexer_mfma(torch, csa, wl, dev, reps=20, warmup=10):
     return {"workload": s.name, "kernel": "index_qk_prefill (fp8 64x128)", "us": round(us, 2),
             "flops_per_launch": fl, "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
             "frac": round(tf / MFMA_PEAK_TFLOPS["fp8"], 4),
-            "timing": "mean of %d back-to-back launches after %d warmup launches" % (reps, warmup)}
+            "timing": "mean of %d back-to-back launches after %d warmup launches, %s" % (reps, warmup, SETTLE_NOTE)}
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -1041,7 +1070,8 @@ def main():
     csa.lib()
 
     if args.copy_only:
-        print(json.dumps({"copy_gbs": copy_ceiling(torch, dev), "bytes_per_copy": 2 * (1 << 30)}), flush=True)
+        print(json.dumps({"copy_gbs": copy_ceiling(torch, dev, settle_s=0.0), "bytes_per_copy": 2 * (1 << 30)}),
+              flush=True)
         return
 
     W = args.workload
@@ -1131,6 +1161,19 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
+    # The timed steps: one HIP graph per input set (the library's kernels are
+    # captured on torch's capture stream; they use no memsets), replayed
+    # alternately so consecutive steps read different inputs. Captured first,
+    # so that the clock settle below runs the step itself and no idle gap
+    # (the capture) separates it from the timed regions.
+    graphs = []
+    for k in range(2):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            step(k)
+        graphs.append(gph)
+    settle(torch, lambda k: graphs[k % 2].replay())
+
     # Per-kernel average durations: back-to-back launches of each call (both
     # input sets alternating) between HIP events on the launch stream.
     breakdown = {}
@@ -1146,15 +1189,6 @@ def main():
             torch.cuda.synchronize()
             breakdown[l] = round(1000.0 * e0.elapsed_time(e1) / args.steps, 2)
 
-    # The timed steps: one HIP graph per input set (the library's kernels are
-    # captured on torch's capture stream; they use no memsets), replayed
-    # alternately so consecutive steps read different inputs.
-    graphs = []
-    for k in range(2):
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph):
-            step(k)
-        graphs.append(gph)
     for k in range(args.warmup):
         graphs[k % 2].replay()
     torch.cuda.synchronize()
@@ -1229,7 +1263,7 @@ def main():
         "config": cfg, "roofline": roof,
         "breakdown_us": breakdown,
         "timing": "value/ms_per_step: HIP-graph replays of the whole step; breakdown_us and roofline: "
-                  "back-to-back launches of each call between HIP events",
+                  "back-to-back launches of each call between HIP events; " + SETTLE_NOTE,
         "step_hbm_gbs": round(step_bytes / (ms / 1000.0) / 1e9, 1),
         "step_frac": round(step_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "copy_ceiling_gbs": copy_ceiling(torch, dev),
