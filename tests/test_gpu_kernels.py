@@ -356,7 +356,9 @@ def test_sparse_attn(fmt, B, Lq, H, D, k, W, sink):
 
 
 @pytest.mark.parametrize("B,Lq,H,k,W,q_pos0,sink", [
-    (1, 1, 32, 1024, 128, 8000, True),     # 1152 sources: two staged V blocks
+    (1, 1, 32, 1024, 128, 8000, True),     # 1152 sources: 32-dim P V slices, all 1152 rows staged at once
+    (20, 1, 16, 1024, 128, 6000, True),    # 20 rows: 32-dim slices, two staged blocks (640 + 512 rows)
+    (33, 1, 16, 600, 100, 3000, True),     # 33 rows: 64-dim slices, two staged blocks (640 + 64 rows)
     (2, 2, 48, 200, 128, 50, True),        # window cut at t = 50 < W, padded idx
     (1, 2, 128, 300, 40, 5000, False),     # 128 heads, no sink
     (3, 1, 16, 64, 0, 900, True),          # compressed only
