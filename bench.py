@@ -1019,11 +1019,13 @@ def _cpu_model():
 
 
 def _sample(parts, seconds, query_fn):
+    """Oracle query tokens until `seconds` of oracle work: the batch's tokens
+    in order, cycled when one pass takes less. Returns (tokens, seconds)."""
     B = parts[0][0].B
     done, spent = 0, 0.0
-    while done < B and (done == 0 or spent < seconds):
+    while done == 0 or spent < seconds:
         for s, x in parts:
-            spent += query_fn(s, x, done) if query_fn else _oracle_query(s, x, done)
+            spent += query_fn(s, x, done % B) if query_fn else _oracle_query(s, x, done % B)
         done += 1
     return done, spent
 
@@ -1042,11 +1044,11 @@ def cpu_baseline(wl_name, parts, seconds, query_fn=None):
         with threadpool_limits(limits=1):
             d1, s1 = _sample(parts, seconds, query_fn)
         one = {"value": round(d1 / s1, 4), "cores": 1,
-               "sample": "%d of %d query tokens, %.1f s of oracle work" % (d1, B, s1)}
+               "sample": "%d query tokens (the batch's %d in order, cycled), %.1f s of oracle work" % (d1, B, s1)}
     except ImportError:
         pass
     return {"value": round(done / spent, 4), "unit": "query-tok/s", "cores": cores, "kind": "oracle",
-            "sample": "%d of %d query tokens of %s, %.1f s of oracle work (numpy float64, BLAS threads %d; "
+            "sample": "%d query tokens (the batch's %d in order, cycled) of %s, %.1f s of oracle work (numpy float64, BLAS threads %d; "
                       "host has %d CPUs: %s)" % (done, B, wl_name, spent, cores, os.cpu_count(), _cpu_model()),
             "one_thread": one}
 
